@@ -1,0 +1,20 @@
+"""CPU oracle for the QSA hot path -- test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  It shares no code with the HIP library
+and never calls it.  See ``qsa_oracle.c`` for the definitions it follows.
+"""
+from .oracle import (  # noqa: F401
+    build,
+    load,
+    pool,
+    rope_rows,
+    scores,
+    select,
+    score_rows,
+    k_blocks,
+    index_rows,
+    attend_rows,
+    prefill_rows,
+    decode,
+)
