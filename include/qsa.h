@@ -1,0 +1,188 @@
+/*
+ * qsa.h -- C ABI of the MI355X (gfx950) Qwen Sparse Attention (QSA) hot path.
+ *
+ * The method (cited by site and section; every page describes the report
+ * "On the Design of Qwen3.8-Next Architecture: Evaluation, Efficiency, and
+ * Training Stability"):
+ *   [hub]   gunjandhanuka.github.io research-hub note, "Key ideas", the QSA
+ *           compressed-indexer bullet: MQA indexer with 4 query heads and one
+ *           shared 128-dim key head; keys average-pooled into blocks of r;
+ *           partial RoPE (64 of 128 dims) after compression;
+ *           I_ib = sum_h ReLU(<q_i^h, kbar_b>); top-k_B = ceil(K/r) blocks
+ *           plus the current-block tail; K = 2048, r = 4.
+ *   [glide] paperglide.net reader, section "Qwen Sparse Attention": toy
+ *           walk-through (pool, block-causal scores, top-K_B, expansion to
+ *           token indices, incomplete-block tail) and Figure 3 (indexer ->
+ *           top-k indices -> micro-block sparse mask -> sparse core
+ *           attention); section "QSA Ablations and Efficiency", Figure 6
+ *           (prefill and decode kernels: indexer + sparse core attention).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor arguments are caller-owned DEVICE pointers, contiguous,
+ *     16-byte aligned, in the layouts stated per argument (row-major, the
+ *     last index fastest).  `dtype` selects float32 or bfloat16 storage for
+ *     every floating-point tensor of the call; indices are int32.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call
+ *     validates its arguments on the host, enqueues its kernels on `stream`
+ *     and returns without synchronising.  Kernel faults surface at the
+ *     caller's next synchronisation.
+ *   - The library allocates no device memory.  Scratch memory comes only
+ *     from the `workspace` arguments, sized by the *_workspace functions;
+ *     its contents need no initialisation and are not preserved.
+ *   - On error a call returns a non-zero qsa_status, launches nothing,
+ *     writes no output, and records a message for qsa_last_error() (per host
+ *     thread).  No C++ exception crosses this boundary.
+ *   - Positions: query row t of sequence b sits at token position
+ *     p = q_pos0 + t (prefill), or p = d_seq_len[b] - n_q + t when the
+ *     device array d_seq_len is given (decode: the new tokens are already
+ *     in the caches).  Block b is visible to position p iff (b+1)r-1 <= p.
+ *   - Inputs must be finite; NaN or Inf give undefined selections.
+ *   - Results are deterministic: identical inputs give identical bits.
+ *   - Supported shapes: r = 4, h_idx = 4, d_idx = 128, rope_dims even and
+ *     <= 128, K >= r, head dim d = 128, hq % hkv == 0, hq / hkv <= 16.
+ *     Other values return QSA_ERR_UNSUPPORTED.
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QSA_OK = 0,
+  QSA_ERR_NULL = 1,        /* a required pointer is NULL */
+  QSA_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes */
+  QSA_ERR_DTYPE = 3,       /* unknown dtype */
+  QSA_ERR_UNSUPPORTED = 4, /* valid by the method, not built here */
+  QSA_ERR_WORKSPACE = 5,   /* workspace missing or too small */
+  QSA_ERR_LAUNCH = 6       /* the HIP runtime refused a launch */
+} qsa_status;
+
+typedef enum { QSA_FP32 = 0, QSA_BF16 = 1 } qsa_dtype;
+
+/* Method constants ([hub]): defaults r = 4, K = 2048 (k_B = 512),
+ * h_idx = 4, d_idx = 128, rope_dims = 64, rope_theta = 10000. */
+typedef struct {
+  int32_t r;         /* micro-block size: tokens per pooled key */
+  int32_t K;         /* token budget; k_B = ceil(K / r) selected blocks */
+  int32_t h_idx;     /* indexer query heads */
+  int32_t d_idx;     /* indexer head dimension */
+  int32_t rope_dims; /* leading indexer dims rotated after pooling */
+  float rope_theta;  /* RoPE base: pair (j, j + rope_dims/2) turns by
+                        p * theta^(-2j / rope_dims) at position p */
+} qsa_params;
+
+/* Fills *p with the defaults above. */
+void qsa_default_params(qsa_params* p);
+
+/* k_B = ceil(K / r): the number of blocks each query selects at most. */
+int32_t qsa_k_blocks(const qsa_params* p);
+
+/* Human-readable name of a status code (static string). */
+const char* qsa_status_str(qsa_status s);
+
+/* Detail of the last error on this host thread ("" if none). */
+const char* qsa_last_error(void);
+
+/*
+ * qsa_pool_keys -- pooled indexer keys ([hub]: average-pool the shared key
+ * head over blocks of r tokens, then partial RoPE after compression;
+ * [glide] toy: block 0 = (k0 + k1) / 2).
+ *
+ *   kbar[b][j][c] = RoPE_{(j+1)r-1}( (1/r) sum_{t<r} k_idx[b][j*r+t][c] )
+ *   for every sequence b < B and block j in [block_begin, block_end); RoPE
+ *   acts on dims c < rope_dims only.  Result rounded (nearest-even) to dtype.
+ *
+ *   k_idx : [B][n_cap][d_idx]   indexer keys of every token
+ *   kbar  : [B][nb_cap][d_idx]  pooled key cache (rows outside the range
+ *                               are left untouched)
+ * Errors: NULL pointers; block_end * r > n_cap or block_end > nb_cap or
+ * block_begin > block_end -> QSA_ERR_SHAPE.
+ */
+qsa_status qsa_pool_keys(const qsa_params* p, qsa_dtype dtype, const void* k_idx, int64_t n_cap,
+                         void* kbar, int64_t nb_cap, int32_t B, int64_t block_begin,
+                         int64_t block_end, void* stream);
+
+/*
+ * qsa_index_topk -- compressed MQA indexer and top-k_B block selection
+ * ([hub]: I_ib = sum_h ReLU(<q_i^h, kbar_b>) with partial RoPE on the query
+ * at its position, top-k_B = ceil(K/r); [glide]: the compressed causal mask,
+ * "select the top K_B blocks per query").
+ *
+ * For each query row: the min(k_B, visible) blocks with the largest score
+ * under the total order (score descending, block id ascending), written as
+ * ascending block ids, padded with -1.  The score matrix is never stored.
+ *
+ *   q_idx : [B][n_q][h_idx][d_idx]  indexer queries, NOT rotated
+ *   kbar  : [B][nb_cap][d_idx]      pooled keys from qsa_pool_keys
+ *   d_seq_len : NULL (prefill: positions q_pos0 + t) or device int32 [B]
+ *               (decode: positions d_seq_len[b] - n_q + t)
+ *   idx   : [B][n_q][k_B] int32 out;  cnt : [B][n_q] int32 out
+ *   workspace : device scratch of qsa_index_topk_workspace(...) bytes
+ * Errors: NULL pointers; n_q < 1; a prefill position beyond nb_cap * r
+ * -> QSA_ERR_SHAPE; workspace too small -> QSA_ERR_WORKSPACE.  In decode
+ * mode every d_seq_len[b] must lie in [n_q, nb_cap * r] (not checked on the
+ * host: the values live on the device).
+ */
+qsa_status qsa_index_topk(const qsa_params* p, qsa_dtype dtype, const void* q_idx,
+                          const void* kbar, int64_t nb_cap, int32_t B, int32_t n_q,
+                          int64_t q_pos0, const int32_t* d_seq_len, int32_t* idx, int32_t* cnt,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes qsa_index_topk needs for these sizes on the current
+ * device (decode != 0 when d_seq_len will be given). */
+size_t qsa_index_topk_workspace(const qsa_params* p, qsa_dtype dtype, int32_t B, int32_t n_q,
+                                int64_t nb_cap, int32_t decode);
+
+/*
+ * qsa_sparse_attn_prefill -- sparse core attention ([glide] Figure 3: the
+ * selected blocks expanded to tokens, joined with the incomplete-block tail;
+ * each query attends to that set only).
+ *
+ *   T_i = { j*r + u : j in idx[b][t][0..cnt), u < r } U { floor((p+1)/r)*r .. p }
+ *   out[b][t][h] = sum_{s in T_i} softmax_s(scale <q[b][t][h], k[b][g][s]>) v[b][g][s]
+ *   with g = floor(h * hkv / hq); scale <= 0 means 1/sqrt(d).
+ *
+ *   q   : [B][n_q][hq][d];  k, v : [B][hkv][n_cap][d] (head-major caches)
+ *   idx, cnt : from qsa_index_topk (same n_q, positions)
+ *   out : [B][n_q][hq][d]
+ * Errors: NULL pointers; q_pos0 + n_q > n_cap -> QSA_ERR_SHAPE; d != 128 or
+ * hq / hkv > 16 -> QSA_ERR_UNSUPPORTED.
+ */
+qsa_status qsa_sparse_attn_prefill(const qsa_params* p, qsa_dtype dtype, const void* q,
+                                   const void* k, const void* v, int64_t n_cap,
+                                   const int32_t* idx, const int32_t* cnt, int32_t B,
+                                   int32_t n_q, int64_t q_pos0, int32_t hq, int32_t hkv,
+                                   int32_t d, float scale, void* out, void* stream);
+
+/*
+ * qsa_sparse_attn_decode -- the same attention for n_q new tokens per
+ * sequence against the KV caches (the pages' decode benchmark, Figure 6(d),
+ * uses next_n = 4), split over the selected blocks and combined
+ * (flash-decoding).  Positions d_seq_len[b] - n_q + t.
+ *
+ *   q : [B][n_q][hq][d]; k_cache, v_cache : [B][hkv][n_cap][d];
+ *   d_seq_len : device int32 [B], includes the new tokens;
+ *   idx, cnt : from qsa_index_topk in decode mode; out : [B][n_q][hq][d]
+ *   workspace : qsa_sparse_attn_decode_workspace(...) bytes
+ * Errors as for the prefill call, plus QSA_ERR_WORKSPACE.
+ */
+qsa_status qsa_sparse_attn_decode(const qsa_params* p, qsa_dtype dtype, const void* q,
+                                  const void* k_cache, const void* v_cache, int64_t n_cap,
+                                  const int32_t* d_seq_len, const int32_t* idx,
+                                  const int32_t* cnt, int32_t B, int32_t n_q, int32_t hq,
+                                  int32_t hkv, int32_t d, float scale, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+size_t qsa_sparse_attn_decode_workspace(const qsa_params* p, int32_t B, int32_t n_q, int32_t hq,
+                                        int32_t hkv, int32_t d);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

@@ -1,0 +1,89 @@
+"""The C-ABI library loads and exports every entry point include/qsa.h
+declares; host-side validation rejects bad arguments before any launch (no
+GPU needed: every case below fails validation on the host)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from trainable_sparse_attention_amd import qsa
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                   "qsa.h")
+
+
+def _declared():
+    src = open(HDR).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qsa_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert sorted(qsa.EXPORTS) == _declared()
+
+
+def test_library_exports_every_declared_symbol():
+    lib = qsa.lib()
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_defaults_and_status_strings():
+    lib = qsa.lib()
+    p = qsa.Params()
+    lib.qsa_default_params(ctypes.byref(p))
+    assert (p.r, p.K, p.h_idx, p.d_idx, p.rope_dims, p.rope_theta) == (4, 2048, 4, 128, 64, 10000.0)
+    assert qsa.k_blocks(p) == 512
+    for code, name in qsa.STATUS.items():
+        assert lib.qsa_status_str(code).decode() == name
+
+
+def _expect(status, code, lib):
+    assert status == code, (qsa.STATUS.get(status), lib.qsa_last_error().decode())
+    assert lib.qsa_last_error().decode() != ""
+
+
+def test_host_validation_errors():
+    lib = qsa.lib()
+    p = qsa.params()
+    P = ctypes.byref(p)
+    fake = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    _expect(lib.qsa_pool_keys(P, 1, None, 64, fake, 16, 1, 0, 16, None), 1, lib)
+    _expect(lib.qsa_pool_keys(P, 7, fake, 64, fake, 16, 1, 0, 16, None), 3, lib)
+    _expect(lib.qsa_pool_keys(P, 1, fake, 60, fake, 16, 1, 0, 16, None), 2, lib)
+    _expect(lib.qsa_pool_keys(P, 1, fake, 64, fake, 15, 1, 0, 16, None), 2, lib)
+    _expect(lib.qsa_pool_keys(P, 1, fake, 64, fake, 16, 1, 5, 4, None), 2, lib)
+    bad = qsa.params(r=8)
+    _expect(lib.qsa_pool_keys(ctypes.byref(bad), 1, fake, 64, fake, 16, 1, 0, 8, None), 4, lib)
+    _expect(lib.qsa_pool_keys(None, 1, fake, 64, fake, 16, 1, 0, 8, None), 1, lib)
+    # index: too few blocks for the positions; workspace missing; n_q < 1
+    _expect(lib.qsa_index_topk(P, 1, fake, fake, 10, 1, 64, 0, None, fake, fake, fake, 1 << 30,
+                               None), 2, lib)
+    _expect(lib.qsa_index_topk(P, 1, fake, fake, 16, 1, 0, 0, None, fake, fake, fake, 1 << 30,
+                               None), 2, lib)
+    _expect(lib.qsa_index_topk(P, 1, fake, fake, 16, 1, 64, 0, None, fake, fake, None, 0, None),
+            5, lib)
+    # attention: head dim, GQA ratio, positions beyond the cache
+    _expect(lib.qsa_sparse_attn_prefill(P, 1, fake, fake, fake, 64, fake, fake, 1, 8, 0, 16, 2,
+                                        64, 0.0, fake, None), 4, lib)
+    _expect(lib.qsa_sparse_attn_prefill(P, 1, fake, fake, fake, 64, fake, fake, 1, 8, 0, 16, 3,
+                                        128, 0.0, fake, None), 2, lib)
+    _expect(lib.qsa_sparse_attn_prefill(P, 1, fake, fake, fake, 64, fake, fake, 1, 8, 0, 64, 2,
+                                        128, 0.0, fake, None), 4, lib)
+    _expect(lib.qsa_sparse_attn_prefill(P, 1, fake, fake, fake, 64, fake, fake, 1, 8, 60, 16, 2,
+                                        128, 0.0, fake, None), 2, lib)
+    _expect(lib.qsa_sparse_attn_decode(P, 1, fake, fake, fake, 64, None, fake, fake, 1, 1, 16, 2,
+                                       128, 0.0, fake, fake, 1 << 30, None), 1, lib)
+    _expect(lib.qsa_sparse_attn_decode(P, 1, fake, fake, fake, 64, fake, fake, fake, 1, 1, 16, 2,
+                                       128, 0.0, fake, fake, 0, None), 5, lib)
+
+
+def test_workspace_sizes_grow_with_work():
+    p = qsa.params()
+    a = qsa.qsa_index_topk_workspace(p, 1, 1, 4096, 1024, False)
+    b = qsa.qsa_index_topk_workspace(p, 1, 1, 1 << 18, 1 << 16, False)
+    assert 0 < a <= b
+    d = qsa.qsa_index_topk_workspace(p, 1, 8, 1, 1 << 18, True)
+    assert d >= 8 * (1 << 18) * 4  # one score per block per sequence
+    assert qsa.qsa_sparse_attn_decode_workspace(p, 8, 1, 16, 2) > 0

@@ -1,0 +1,313 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Stage isolation: each GPU stage is compared with the oracle stage fed the
+same bytes the GPU stage read (the oracle selects on the GPU's pooled keys;
+the oracle attends with the GPU's selection), so a near-tie difference in
+one stage cannot leak into the next.  Sets use the near-tie rule and outputs
+the max-abs relative error of tests/parity.py.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.parity import TOL, as_f64, check_sets, rel_err, to_dev, to_host
+from trainable_sparse_attention_amd import inputs, qsa
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+def _params(K=2048, rope_dims=64):
+    return qsa.params(K=K, rope_dims=rope_dims)
+
+
+def _dev_inputs(d):
+    return {k: to_dev(d[k]) for k in ("q_idx", "k_idx", "q", "k", "v")}
+
+
+def _pool_gpu(p, k_idx, nb):
+    kbar = torch.empty((k_idx.shape[0], nb, 128), dtype=k_idx.dtype, device=k_idx.device)
+    qsa.qsa_pool_keys(p, k_idx, kbar, 0, nb)
+    return kbar
+
+
+def _index_gpu(p, q_idx, kbar, q_pos0=0, seq_len=None):
+    B, n_q = q_idx.shape[:2]
+    kB = qsa.k_blocks(p)
+    idx = torch.full((B, n_q, kB), -7, dtype=torch.int32, device=q_idx.device)
+    cnt = torch.full((B, n_q), -7, dtype=torch.int32, device=q_idx.device)
+    ws = qsa.workspace(qsa.qsa_index_topk_workspace(p, qsa.dtype_code(q_idx), B, n_q,
+                                                    kbar.shape[1], seq_len is not None))
+    qsa.qsa_index_topk(p, q_idx, kbar, idx, cnt, ws, q_pos0, seq_len)
+    return idx, cnt
+
+
+def _attn_gpu(p, q, k, v, idx, cnt, q_pos0=0):
+    out = torch.empty_like(q)
+    qsa.qsa_sparse_attn_prefill(p, q, k, v, idx, cnt, out, q_pos0)
+    return out
+
+
+def _check_index_rows(b, rows, g_idx, g_cnt, q_idx_h, kbar_h, K, q_pos0=0, rope_dims=64):
+    o_idx, o_cnt = oracle.index_rows(q_idx_h, kbar_h, rows, q_pos0, K=K, rope_dims=rope_dims)
+    gi, gc = g_idx[b][rows], g_cnt[b][rows]
+    differ = [u for u in range(len(rows)) if not np.array_equal(gi[u], o_idx[u])]
+    scores = [None] * len(rows)
+    if differ:
+        sc = oracle.score_rows(q_idx_h, kbar_h, [rows[u] for u in differ], q_pos0,
+                               rope_dims=rope_dims)
+        for j, u in enumerate(differ):
+            scores[u] = sc[j]
+    sub = differ if differ else []
+    assert np.array_equal(gc, o_cnt), "counts differ"
+    near = check_sets(gi[sub], gc[sub], o_idx[sub], o_cnt[sub], [scores[u] for u in sub])
+    return near, o_idx, o_cnt
+
+
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_pool_parity(dtype):
+    say("pool", dtype)
+    d = inputs.small(B=2, n=1030, dtype=dtype, seed=21)
+    p = _params()
+    k_idx = to_dev(d["k_idx"])
+    nb = 1030 // 4
+    kbar = torch.zeros((2, nb + 3, 128), dtype=k_idx.dtype, device="cuda")
+    qsa.qsa_pool_keys(p, k_idx, kbar, 0, 100)
+    qsa.qsa_pool_keys(p, k_idx, kbar, 100, nb)
+    torch.cuda.synchronize()
+    got = to_host(kbar)
+    for b in range(2):
+        ref = oracle.pool(d["k_idx"][b])
+        g, o = as_f64(got[b, :nb]), as_f64(ref)
+        if dtype == "bf16":
+            ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(o), 1e-30))) - 7)
+            assert np.all(np.abs(g - o) <= ulp), np.max(np.abs(g - o) / ulp)
+        else:
+            scale = np.max(np.abs(o), axis=1, keepdims=True)
+            assert np.all(np.abs(g - o) <= 4 * 2.0 ** -24 * scale)
+        assert np.all(got[b, nb:] == 0), "rows beyond the range were written"
+
+
+def test_cfg0_end_to_end_all_rows():
+    """configuration 0 (n=4096, float32, 4 q heads / 1 kv head, 16 planted)."""
+    say("cfg0 end to end")
+    d = inputs.make("cfg0", seed=100)
+    p = _params()
+    t = _dev_inputs(d)
+    kbar = _pool_gpu(p, t["k_idx"], 1024)
+    idx, cnt = _index_gpu(p, t["q_idx"], kbar)
+    out = _attn_gpu(p, t["q"], t["k"], t["v"], idx, cnt)
+    torch.cuda.synchronize()
+    kbar_h, g_idx, g_cnt, g_out = to_host(kbar), to_host(idx), to_host(cnt), to_host(out)
+    # pool stage
+    ref = oracle.pool(d["k_idx"][0])
+    np.testing.assert_allclose(kbar_h[0], ref, rtol=0, atol=4 * 2.0 ** -24 * np.abs(ref).max())
+    rows = np.arange(4096)
+    near, _, _ = _check_index_rows(0, rows, g_idx, g_cnt, d["q_idx"][0], kbar_h[0], 2048)
+    say("cfg0 near-tie differences:", near)
+    for (_, i, blk, *_r) in d["plants"]:
+        assert blk in set(g_idx[0, i, :g_cnt[0, i]].tolist())
+    o = oracle.attend_rows(d["q"][0], d["k"][0], d["v"][0], rows, g_idx[0], g_cnt[0])
+    err = rel_err(g_out[0], o)
+    say("cfg0 attention rel err", err)
+    assert err <= TOL["fp32"]
+
+
+@pytest.mark.parametrize("n,dtype,K", [(1, "fp32", 16), (3, "bf16", 16), (5, "fp32", 8),
+                                       (130, "bf16", 16), (1003, "fp32", 64),
+                                       (1003, "bf16", 2048), (2500, "bf16", 100)])
+def test_small_and_ragged(n, dtype, K):
+    say("small/ragged n=%d %s K=%d" % (n, dtype, K))
+    d = inputs.small(B=2, n=n, hq=8, hkv=2, dtype=dtype, K=K, seed=n)
+    p = _params(K=K)
+    t = _dev_inputs(d)
+    nb = n // 4
+    kbar = _pool_gpu(p, t["k_idx"], max(nb, 1)) if nb else torch.zeros(
+        (2, 1, 128), dtype=t["k_idx"].dtype, device="cuda")
+    idx, cnt = _index_gpu(p, t["q_idx"], kbar)
+    out = _attn_gpu(p, t["q"], t["k"], t["v"], idx, cnt)
+    torch.cuda.synchronize()
+    kbar_h, g_idx, g_cnt, g_out = to_host(kbar), to_host(idx), to_host(cnt), to_host(out)
+    rows = np.arange(n)
+    for b in range(2):
+        _check_index_rows(b, rows, g_idx, g_cnt, d["q_idx"][b], kbar_h[b], K)
+        o = oracle.attend_rows(d["q"][b], d["k"][b], d["v"][b], rows, g_idx[b], g_cnt[b])
+        assert rel_err(g_out[b], o) <= TOL[dtype]
+
+
+def test_large_K_is_dense():
+    say("K >= n: dense causal")
+    n = 600
+    d = inputs.small(B=1, n=n, hq=16, hkv=2, dtype="bf16", K=4096, seed=5)
+    p = _params(K=4096)
+    t = _dev_inputs(d)
+    kbar = _pool_gpu(p, t["k_idx"], n // 4)
+    idx, cnt = _index_gpu(p, t["q_idx"], kbar)
+    out = _attn_gpu(p, t["q"], t["k"], t["v"], idx, cnt)
+    torch.cuda.synchronize()
+    g_idx, g_cnt = to_host(idx)[0], to_host(cnt)[0]
+    for i in range(n):
+        nb = (i + 1) // 4
+        assert g_cnt[i] == nb and np.array_equal(g_idx[i, :nb], np.arange(nb))
+    rows = np.arange(n)
+    o = oracle.attend_rows(d["q"][0], d["k"][0], d["v"][0], rows, g_idx, g_cnt)
+    assert rel_err(to_host(out)[0], o) <= TOL["bf16"]
+
+
+def test_bf16_medium_end_to_end_and_chunking():
+    """n=16384, two sequences, 16 q / 2 kv heads, planted matches; chunked
+    prefill (two halves through q_pos0) equals the full run bit for bit."""
+    say("bf16 medium")
+    n = 16384
+    d = inputs.small(B=2, n=n, hq=16, hkv=2, dtype="bf16", planted=32, seed=33)
+    p = _params()
+    t = _dev_inputs(d)
+    kbar = _pool_gpu(p, t["k_idx"], n // 4)
+    idx, cnt = _index_gpu(p, t["q_idx"], kbar)
+    out = _attn_gpu(p, t["q"], t["k"], t["v"], idx, cnt)
+    # second half as its own chunk
+    h = n // 2
+    idx2, cnt2 = _index_gpu(p, t["q_idx"][:, h:].contiguous(), kbar, q_pos0=h)
+    out2 = _attn_gpu(p, t["q"][:, h:].contiguous(), t["k"], t["v"], idx2, cnt2, q_pos0=h)
+    # determinism
+    idx3, cnt3 = _index_gpu(p, t["q_idx"], kbar)
+    out3 = _attn_gpu(p, t["q"], t["k"], t["v"], idx3, cnt3)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx3) and torch.equal(cnt, cnt3) and torch.equal(out, out3)
+    assert torch.equal(idx[:, h:], idx2) and torch.equal(cnt[:, h:], cnt2)
+    assert torch.equal(out[:, h:], out2)
+    kbar_h, g_idx, g_cnt, g_out = to_host(kbar), to_host(idx), to_host(cnt), to_host(out)
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(2040, 2062),
+                                     rng.integers(0, n, 256), np.arange(n - 8, n),
+                                     [pl[1] for pl in d["plants"]]]))
+    for b in range(2):
+        near, _, _ = _check_index_rows(b, rows, g_idx, g_cnt, d["q_idx"][b], kbar_h[b], 2048)
+        say("medium seq", b, "near-tie differences", near)
+        o = oracle.attend_rows(d["q"][b], d["k"][b], d["v"][b], rows, g_idx[b][rows],
+                               g_cnt[b][rows])
+        err = rel_err(g_out[b][rows], o)
+        say("medium seq", b, "attention rel err", err)
+        assert err <= TOL["bf16"]
+    for (b, i, blk, *_r) in d["plants"]:
+        assert blk in set(g_idx[b, i, :g_cnt[b, i]].tolist())
+
+
+@pytest.mark.parametrize("n_q,dtype", [(1, "bf16"), (4, "bf16"), (1, "fp32"), (6, "bf16")])
+def test_decode_parity(n_q, dtype):
+    """Ragged sequence lengths; n_q new tokens per sequence (4 = the pages'
+    next_n); decode equals the prefill rows at the same positions."""
+    say("decode n_q=%d %s" % (n_q, dtype))
+    lens = [9000, 9001, 5003]
+    n = max(lens)
+    d = inputs.small(B=3, n=n, hq=16, hkv=2, dtype=dtype, seed=40 + n_q)
+    p = _params()
+    t = _dev_inputs(d)
+    nbc = n // 4
+    kbar = _pool_gpu(p, t["k_idx"], nbc)
+    seq_len = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    qi = torch.stack([t["q_idx"][b, L - n_q:L] for b, L in enumerate(lens)]).contiguous()
+    qq = torch.stack([t["q"][b, L - n_q:L] for b, L in enumerate(lens)]).contiguous()
+    idx, cnt = _index_gpu(p, qi, kbar, seq_len=seq_len)
+    out = torch.empty_like(qq)
+    ws = qsa.workspace(qsa.qsa_sparse_attn_decode_workspace(p, 3, n_q, 16, 2))
+    qsa.qsa_sparse_attn_decode(p, qq, t["k"], t["v"], seq_len, idx, cnt, out, ws)
+    # the same rows through the prefill entry points
+    pidx, pcnt = _index_gpu(p, t["q_idx"], kbar)
+    torch.cuda.synchronize()
+    kbar_h, g_idx, g_cnt, g_out = to_host(kbar), to_host(idx), to_host(cnt), to_host(out)
+    p_idx, p_cnt = to_host(pidx), to_host(pcnt)
+    for b, L in enumerate(lens):
+        rows = np.arange(L - n_q, L)
+        assert np.array_equal(g_idx[b], p_idx[b][rows]) and np.array_equal(g_cnt[b], p_cnt[b][rows])
+        o_idx, o_cnt = oracle.index_rows(d["q_idx"][b], kbar_h[b], rows)
+        sc = oracle.score_rows(d["q_idx"][b], kbar_h[b], rows)
+        check_sets(g_idx[b], g_cnt[b], o_idx, o_cnt, sc)
+        o = oracle.attend_rows(d["q"][b], d["k"][b], d["v"][b], rows, g_idx[b], g_cnt[b])
+        assert rel_err(g_out[b], o) <= TOL[dtype]
+
+
+# ---- full-size configurations, sampled rows --------------------------------
+
+def _sample_rows(n, plants, seed=0, nrand=96):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([np.arange(8), np.arange(2040, 2062), rng.integers(0, n, nrand),
+                                     np.arange(n - 8, n), [pl[1] for pl in plants[:16]]]))
+
+
+@pytest.mark.parametrize("cfg", ["cfg1", "cfg2"])
+def test_full_size_prefill_sampled(cfg):
+    say("full-size prefill", cfg)
+    d = inputs.make(cfg, seed=100 + int(cfg[-1]), backend="torch")
+    p = _params()
+    n = d["n"]
+    kbar, idx, cnt, out = qsa.prefill(p, d["k_idx"], d["q_idx"], d["q"], d["k"], d["v"])
+    torch.cuda.synchronize()
+    rows = _sample_rows(n, d["plants"])
+    rt = torch.from_numpy(rows).cuda()
+    kbar_h = to_host(kbar[0])
+    qi_h = to_host(d["q_idx"][0][rt])
+    g_idx, g_cnt = to_host(idx[0][rt]), to_host(cnt[0][rt])
+    # oracle on the sampled rows: rows are re-indexed 0..len-1, positions kept
+    o_idx = np.empty_like(g_idx)
+    o_cnt = np.empty_like(g_cnt)
+    sc = []
+    for u, i in enumerate(rows):
+        oi, oc = oracle.index_rows(qi_h[u:u + 1], kbar_h, [0], int(i))
+        o_idx[u], o_cnt[u] = oi[0], oc[0]
+        sc.append(oracle.score_rows(qi_h[u:u + 1], kbar_h, [0], int(i))[0])
+    near = check_sets(g_idx, g_cnt, o_idx, o_cnt, sc)
+    say(cfg, "near-tie differences", near)
+    for (_, i, blk, *_r) in d["plants"][:16]:
+        u = int(np.nonzero(rows == i)[0][0])
+        assert blk in set(g_idx[u, :g_cnt[u]].tolist())
+    k_h, v_h = to_host(d["k"][0]), to_host(d["v"][0])
+    q_h = to_host(d["q"][0][rt])
+    errs = []
+    for u, i in enumerate(rows):
+        o = oracle.attend_rows(q_h[u:u + 1], k_h, v_h, [0], g_idx[u:u + 1], g_cnt[u:u + 1],
+                               pos0=int(i))
+        errs.append((as_f64(to_host(out[0][int(i)])), o[0]))
+    err = rel_err(np.stack([e[0] for e in errs]), np.stack([e[1] for e in errs]))
+    say(cfg, "attention rel err", err)
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("cfg,check", [("cfg3", [0, 63]), ("cfg4d", [0, 7])])
+def test_full_size_decode_sampled(cfg, check):
+    say("full-size decode", cfg)
+    d = inputs.make(cfg, seed=100 + int(cfg[3]), backend="torch")
+    p = _params()
+    B, L = d["B"], d["n"]
+    nb = L // 4
+    kbar = _pool_gpu(p, d["k_idx"], nb)
+    seq_len = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    idx, cnt = _index_gpu(p, d["q_idx"], kbar, seq_len=seq_len)
+    out = torch.empty_like(d["q"])
+    ws = qsa.workspace(qsa.qsa_sparse_attn_decode_workspace(p, B, 1, 16, 2))
+    qsa.qsa_sparse_attn_decode(p, d["q"], d["k"], d["v"], seq_len, idx, cnt, out, ws)
+    torch.cuda.synchronize()
+    for b in check:
+        kbar_h = to_host(kbar[b])
+        qi = to_host(d["q_idx"][b, 0])
+        o_idx, o_cnt = oracle.index_rows(qi[None], kbar_h, [0], L - 1)
+        sc = oracle.score_rows(qi[None], kbar_h, [0], L - 1)
+        g_idx, g_cnt = to_host(idx[b]), to_host(cnt[b])
+        check_sets(g_idx, g_cnt, o_idx, o_cnt, sc)
+        for (bb, i, blk, *_r) in d["plants"]:
+            if bb == b:
+                assert blk in set(g_idx[0, :g_cnt[0]].tolist())
+        o = oracle.attend_rows(to_host(d["q"][b]), to_host(d["k"][b]), to_host(d["v"][b]), [0],
+                               g_idx, g_cnt, pos0=L - 1)
+        err = rel_err(to_host(out[b]), o)
+        say(cfg, "seq", b, "attention rel err", err)
+        assert err <= TOL["bf16"]

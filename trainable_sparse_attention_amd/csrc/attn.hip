@@ -1,0 +1,439 @@
+// Sparse core attention over gathered micro-blocks (paperglide reader,
+// "Qwen Sparse Attention", Figure 3: selected block indices expanded into a
+// micro-block sparse mask; the incomplete-block tail is always attended).
+//
+// One 64-lane wave handles one (sequence, query row, KV head, split) and the
+// hq/hkv query heads that share the KV head (GQA).  The token set is walked
+// in chunks of 8 slots (a slot is one selected block of r = 4 keys, or the
+// tail); each chunk gathers 8 KB of K and 8 KB of V (1 KB contiguous per
+// block per head in the head-major caches).
+//
+// bf16: S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 (16 keys x
+//   16 heads per tile, heads beyond hq/hkv are zero); V is staged through
+//   LDS and read transposed for the A operand.  Softmax and accumulation in
+//   float (online, base 2).  P is rounded to bf16 for the PV product.
+// fp32: the same on v_mfma_f32_16x16x4f32, whose one-element-per-lane
+//   operands need no transpose (the output dims are permuted instead).
+//
+// Decode splits the slots over `nsplit` waves per (row, KV head) and writes
+// partial (max, sum, unnormalised output) that attn_combine merges.
+#include <math.h>
+
+#include "qsa_internal.h"
+
+namespace qsa {
+
+namespace {
+
+constexpr int kSlotsPerChunk = 8;
+constexpr int kVRow = 128 + 8;  // LDS row of V in bf16 elements (16 B pad)
+
+struct Row {
+  int64_t pos;
+  int64_t nb;
+  int ntail;
+  int cnt;
+  int nslots;
+  const int32_t* ids;
+};
+
+__device__ __forceinline__ Row row_ctx(const AttnArgs& a, int b, int t) {
+  Row R;
+  R.pos = a.seq_len ? (int64_t)a.seq_len[b] - a.n_q + t : a.q_pos0 + t;
+  R.nb = (R.pos + 1) / a.r;
+  R.ntail = (int)(R.pos + 1 - R.nb * a.r);
+  R.cnt = a.cnt[(int64_t)b * a.n_q + t];
+  R.nslots = R.cnt + (R.ntail > 0 ? 1 : 0);
+  R.ids = a.idx + ((int64_t)b * a.n_q + t) * a.kB;
+  return R;
+}
+
+// Token row of key `tok` (< r) of slot u; false if the key is not in T_i.
+__device__ __forceinline__ bool slot_row(const Row& R, int u, int s1, int tok, int r,
+                                         int64_t* row) {
+  if (u >= s1) {
+    *row = 0;
+    return false;
+  }
+  if (u < R.cnt) {
+    *row = (int64_t)R.ids[u] * r + tok;
+    return true;
+  }
+  *row = R.nb * r + tok;  // tail slot
+  const bool ok = tok < R.ntail;
+  if (!ok) *row = 0;
+  return ok;
+}
+
+__device__ __forceinline__ float wave_max_xor(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float wave_sum_xor(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ void decode_job(const AttnArgs& a, int nsplit, int* b, int* t, int* g,
+                                           int* split) {
+  int64_t w = blockIdx.x;
+  *split = (int)(w % nsplit);
+  w /= nsplit;
+  *g = (int)(w % a.hkv);
+  w /= a.hkv;
+  *t = (int)(w % a.n_q);
+  *b = (int)(w / a.n_q);
+}
+
+}  // namespace
+
+// part layout per (b, t, g, split): m[16], l[16], o[16][128] floats.
+constexpr int kPartFloats = 16 + 16 + 16 * 128;
+
+__global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, float* part) {
+  __shared__ __attribute__((aligned(16))) unsigned short vs[32 * kVRow];
+  const int lane = threadIdx.x;
+  const int hl = lane & 15, gq = lane >> 4;
+  int b, t, g, split;
+  decode_job(a, nsplit, &b, &t, &g, &split);
+  const Row R = row_ctx(a, b, t);
+  int s0 = 0, s1 = R.nslots;
+  if (nsplit > 1) {
+    s0 = split * kSlotsPerChunk;
+    s1 = min(R.nslots, s0 + kSlotsPerChunk);
+  }
+  const int G = a.hq / a.hkv;
+  const int head = g * G + hl;
+  const unsigned short* qs = (const unsigned short*)a.q;
+  const unsigned short* ks =
+      (const unsigned short*)a.k + ((int64_t)b * a.hkv + g) * a.n_cap * 128;
+  const unsigned short* vsrc =
+      (const unsigned short*)a.v + ((int64_t)b * a.hkv + g) * a.n_cap * 128;
+
+  bf16x8 qf[4];
+  {
+    const unsigned short* qrow = qs + (((int64_t)b * a.n_q + t) * a.hq + head) * 128;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (hl < G) v = *(const u16x8*)(qrow + 32 * cc + 8 * gq);
+      qf[cc] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  const float sl2 = a.scale * 1.4426950408889634f;
+  f32x4 o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+
+  for (int s = s0; s < s1; s += kSlotsPerChunk) {
+    // K fragments: key row hl of tile kt = slot s + 4kt + hl/4, token hl%4.
+    bf16x8 kf[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      int64_t row;
+      slot_row(R, s + 4 * kt + (hl >> 2), s1, hl & 3, a.r, &row);
+      const unsigned short* kr = ks + row * 128 + 8 * gq;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+        kf[kt][cc] = __builtin_bit_cast(bf16x8, *(const u16x8*)(kr + 32 * cc));
+    }
+    // V chunk to LDS: lane -> key lane/2 (slot s + key/4), half lane%2.
+    {
+      const int kk = lane >> 1;
+      int64_t row;
+      slot_row(R, s + (kk >> 2), s1, kk & 3, a.r, &row);
+      const unsigned short* vr = vsrc + row * 128 + 64 * (lane & 1);
+      unsigned short* dst = vs + kk * kVRow + 64 * (lane & 1);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) *(u16x8*)(dst + 8 * e) = *(const u16x8*)(vr + 8 * e);
+    }
+    // S^T tiles: lane holds head hl, keys 16kt + 4gq + i.
+    f32x4 sacc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt][cc], qf[cc], sacc[kt], 0, 0, 0);
+    }
+    float sv[8];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int u = s + 4 * kt + gq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int64_t row;
+        const bool ok = slot_row(R, u, s1, i, a.r, &row);
+        sv[4 * kt + i] = ok ? sacc[kt][i] * sl2 : -INFINITY;
+      }
+    }
+    float mx = sv[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
+    mx = wave_max_xor(mx);
+    const float mn = fmaxf(m, mx);
+    const float alpha = exp2f(m - mn);
+    float p[8], rs = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      p[j] = exp2f(sv[j] - mn);
+      rs += p[j];
+    }
+    rs = wave_sum_xor(rs);
+    l = l * alpha + rs;
+    m = mn;
+    u16x8 pb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pb[j] = f32_to_bf16(p[j]);
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, pb);
+    __syncthreads();
+    // O^T tile tt: rows dims 16tt + (A row), B = P^T; A row = dim 16tt + hl,
+    // k index 8gq + j <-> key (j < 4 ? 4gq + j : 16 + 4gq + j - 4).
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      u16x8 vv;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int kk = (j < 4) ? (4 * gq + j) : (16 + 4 * gq + j - 4);
+        vv[j] = vs[kk * kVRow + 16 * tt + hl];
+      }
+      o[tt] = o[tt] * alpha;
+      o[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, o[tt],
+                                                      0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  if (nsplit == 1) {
+    if (hl < G) {
+      const float inv = 1.f / l;
+      unsigned short* orow =
+          (unsigned short*)a.out + (((int64_t)b * a.n_q + t) * a.hq + head) * 128;
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        unsigned short w4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w4[i] = f32_to_bf16(o[tt][i] * inv);
+        uint2 pk;
+        pk.x = (unsigned)w4[0] | ((unsigned)w4[1] << 16);
+        pk.y = (unsigned)w4[2] | ((unsigned)w4[3] << 16);
+        *(uint2*)(orow + 16 * tt + 4 * gq) = pk;
+      }
+    }
+  } else {
+    float* pp = part + ((((int64_t)b * a.n_q + t) * a.hkv + g) * nsplit + split) * kPartFloats;
+    if (gq == 0) {
+      pp[hl] = m;
+      pp[16 + hl] = l;
+    }
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+      *(f32x4*)(pp + 32 + hl * 128 + 16 * tt + 4 * gq) = o[tt];
+  }
+}
+
+__global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, int nsplit, float* part) {
+  const int lane = threadIdx.x;
+  const int hl = lane & 15, gq = lane >> 4;
+  int b, t, g, split;
+  decode_job(a, nsplit, &b, &t, &g, &split);
+  const Row R = row_ctx(a, b, t);
+  int s0 = 0, s1 = R.nslots;
+  if (nsplit > 1) {
+    s0 = split * kSlotsPerChunk;
+    s1 = min(R.nslots, s0 + kSlotsPerChunk);
+  }
+  const int G = a.hq / a.hkv;
+  const int head = g * G + hl;
+  const float* ks = (const float*)a.k + ((int64_t)b * a.hkv + g) * a.n_cap * 128;
+  const float* vsrc = (const float*)a.v + ((int64_t)b * a.hkv + g) * a.n_cap * 128;
+
+  // k index of MFMA call cc in lane group gq <-> dim 32 gq + cc.
+  float qr[32];
+  {
+    const float* qrow = (const float*)a.q + (((int64_t)b * a.n_q + t) * a.hq + head) * 128;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (hl < G) v = *(const f32x4*)(qrow + 32 * gq + 4 * e);
+      qr[4 * e + 0] = v[0];
+      qr[4 * e + 1] = v[1];
+      qr[4 * e + 2] = v[2];
+      qr[4 * e + 3] = v[3];
+    }
+  }
+  const float sl2 = a.scale * 1.4426950408889634f;
+  f32x4 o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+
+  for (int s = s0; s < s1; s += kSlotsPerChunk) {
+    f32x4 sacc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      int64_t row;
+      slot_row(R, s + 4 * kt + (hl >> 2), s1, hl & 3, a.r, &row);
+      const float* kr = ks + row * 128 + 32 * gq;
+      sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const f32x4 kv = *(const f32x4*)(kr + 4 * e);
+#pragma unroll
+        for (int z = 0; z < 4; ++z)
+          sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[z], qr[4 * e + z], sacc[kt], 0, 0, 0);
+      }
+    }
+    float sv[8];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int u = s + 4 * kt + gq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int64_t row;
+        const bool ok = slot_row(R, u, s1, i, a.r, &row);
+        sv[4 * kt + i] = ok ? sacc[kt][i] * sl2 : -INFINITY;
+      }
+    }
+    float mx = sv[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
+    mx = wave_max_xor(mx);
+    const float mn = fmaxf(m, mx);
+    const float alpha = exp2f(m - mn);
+    float p[8], rs = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      p[j] = exp2f(sv[j] - mn);
+      rs += p[j];
+    }
+    rs = wave_sum_xor(rs);
+    l = l * alpha + rs;
+    m = mn;
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) o[tt] = o[tt] * alpha;
+    // PV: call cc covers keys key(cc, gq) = cc < 4 ? 4gq + cc : 16 + 4gq + cc - 4;
+    // output tile tt row m <-> dim 8 m + tt, so each lane reads 8 dims of a key.
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+      const int key = (cc < 4) ? (4 * gq + cc) : (16 + 4 * gq + cc - 4);
+      int64_t row;
+      slot_row(R, s + (key >> 2), s1, key & 3, a.r, &row);
+      const float* vr = vsrc + row * 128 + 8 * hl;
+      const f32x4 v0 = *(const f32x4*)vr;
+      const f32x4 v1 = *(const f32x4*)(vr + 4);
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        const float av = tt < 4 ? v0[tt] : v1[tt - 4];
+        o[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, p[cc], o[tt], 0, 0, 0);
+      }
+    }
+  }
+
+  // Output tile tt row 4gq + i <-> dim 8(4gq + i) + tt.
+  if (nsplit == 1) {
+    if (hl < G) {
+      const float inv = 1.f / l;
+      float* orow = (float*)a.out + (((int64_t)b * a.n_q + t) * a.hq + head) * 128;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 lo, hi;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          lo[tt] = o[tt][i] * inv;
+          hi[tt] = o[tt + 4][i] * inv;
+        }
+        *(f32x4*)(orow + 8 * (4 * gq + i)) = lo;
+        *(f32x4*)(orow + 8 * (4 * gq + i) + 4) = hi;
+      }
+    }
+  } else {
+    float* pp = part + ((((int64_t)b * a.n_q + t) * a.hkv + g) * nsplit + split) * kPartFloats;
+    if (gq == 0) {
+      pp[hl] = m;
+      pp[16 + hl] = l;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4 lo, hi;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        lo[tt] = o[tt][i];
+        hi[tt] = o[tt + 4][i];
+      }
+      *(f32x4*)(pp + 32 + hl * 128 + 8 * (4 * gq + i)) = lo;
+      *(f32x4*)(pp + 32 + hl * 128 + 8 * (4 * gq + i) + 4) = hi;
+    }
+  }
+}
+
+// Merge split partials: one 128-thread block per (b, t, query head).
+template <typename T>
+__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, int nsplit,
+                                                           const float* __restrict__ part) {
+  const int dim = threadIdx.x;
+  int64_t w = blockIdx.x;
+  const int h = (int)(w % a.hq);
+  w /= a.hq;
+  const int t = (int)(w % a.n_q);
+  const int b = (int)(w / a.n_q);
+  const int G = a.hq / a.hkv;
+  const int g = h / G, hl = h % G;
+  const float* base = part + (((int64_t)b * a.n_q + t) * a.hkv + g) * nsplit * kPartFloats;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, base[(int64_t)s * kPartFloats + hl]);
+  float L = 0.f, acc = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float* pp = base + (int64_t)s * kPartFloats;
+    const float ms = pp[hl];
+    if (ms == -INFINITY) continue;
+    const float wgt = exp2f(ms - M);
+    L += pp[16 + hl] * wgt;
+    acc += pp[32 + hl * 128 + dim] * wgt;
+  }
+  Elt<T>::st((T*)a.out, (((int64_t)b * a.n_q + t) * a.hq + h) * 128 + dim, acc / L);
+}
+
+static int decode_splits(int kB) { return (kB + 1 + kSlotsPerChunk - 1) / kSlotsPerChunk; }
+
+hipError_t launch_attn_prefill(qsa_dtype dt, const AttnArgs& a, hipStream_t st) {
+  const int64_t waves = (int64_t)a.B * a.n_q * a.hkv;
+  if (waves == 0) return hipSuccess;
+  if (dt == QSA_BF16)
+    hipLaunchKernelGGL(attn_bf16_kernel, dim3((unsigned)waves), dim3(64), 0, st, a, 1,
+                       (float*)nullptr);
+  else
+    hipLaunchKernelGGL(attn_f32_kernel, dim3((unsigned)waves), dim3(64), 0, st, a, 1,
+                       (float*)nullptr);
+  return hipGetLastError();
+}
+
+size_t attn_decode_workspace(int B, int n_q, int hkv, int kB) {
+  return (size_t)B * n_q * hkv * decode_splits(kB) * kPartFloats * sizeof(float);
+}
+
+hipError_t launch_attn_decode(qsa_dtype dt, const AttnArgs& a, void* ws, hipStream_t st) {
+  const int nsplit = decode_splits(a.kB);
+  const int64_t waves = (int64_t)a.B * a.n_q * a.hkv * nsplit;
+  if (waves == 0) return hipSuccess;
+  float* part = (float*)ws;
+  if (dt == QSA_BF16)
+    hipLaunchKernelGGL(attn_bf16_kernel, dim3((unsigned)waves), dim3(64), 0, st, a, nsplit, part);
+  else
+    hipLaunchKernelGGL(attn_f32_kernel, dim3((unsigned)waves), dim3(64), 0, st, a, nsplit, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 cg((unsigned)((int64_t)a.B * a.n_q * a.hq));
+  if (dt == QSA_BF16)
+    hipLaunchKernelGGL(attn_combine_kernel<unsigned short>, cg, dim3(128), 0, st, a, nsplit,
+                       (const float*)part);
+  else
+    hipLaunchKernelGGL(attn_combine_kernel<float>, cg, dim3(128), 0, st, a, nsplit,
+                       (const float*)part);
+  return hipGetLastError();
+}
+
+}  // namespace qsa

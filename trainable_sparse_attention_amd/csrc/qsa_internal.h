@@ -1,0 +1,103 @@
+// Internal declarations shared by the HIP translation units of libqsa.
+// Device helpers (bf16 storage, RoPE angles) and the host-side launchers
+// that the C ABI (abi.hip) calls after validating arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qsa.h"
+
+namespace qsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// ---- bfloat16 storage: values travel as raw 16-bit patterns -------------
+
+__device__ __forceinline__ float bf16_to_f32(unsigned short h) {
+  return __uint_as_float(((unsigned int)h) << 16);
+}
+
+// Round-to-nearest-even float -> bfloat16 bits (finite inputs; NaN kept NaN).
+__device__ __forceinline__ unsigned short f32_to_bf16(float f) {
+  unsigned int u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (unsigned short)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+
+template <typename T> struct Elt;
+template <> struct Elt<float> {
+  __device__ __forceinline__ static float ld(const float* p, int64_t i) { return p[i]; }
+  __device__ __forceinline__ static void st(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Elt<unsigned short> {
+  __device__ __forceinline__ static float ld(const unsigned short* p, int64_t i) {
+    return bf16_to_f32(p[i]);
+  }
+  __device__ __forceinline__ static void st(unsigned short* p, int64_t i, float v) {
+    p[i] = f32_to_bf16(v);
+  }
+};
+
+// ---- RoPE angle ----------------------------------------------------------
+// Pair (j, j + R/2) turns by pos * theta^(-2j/R).  The angle is formed and
+// reduced in double (positions reach 2^20, where float spacing would be
+// 0.06 rad), then cos/sin are taken in double and rounded to float.
+__device__ __forceinline__ void rope_cs(int64_t pos, int j, int R, double log2_theta, float* c,
+                                        float* s) {
+  double inv = exp2(-2.0 * (double)j / (double)R * log2_theta);
+  double a = (double)pos * inv;
+  double sn, cs;
+  sincos(a, &sn, &cs);
+  *c = (float)cs;
+  *s = (float)sn;
+}
+
+// ---- host launchers (defined in the kernel translation units) ------------
+
+hipError_t launch_pool(qsa_dtype dt, const qsa_params& p, const void* k_idx, int64_t n_cap,
+                       void* kbar, int64_t nb_cap, int B, int64_t b0, int64_t b1,
+                       hipStream_t st);
+
+struct IndexArgs {
+  const void* q_idx;
+  const void* kbar;
+  int64_t nb_cap;
+  int B, n_q;
+  int64_t q_pos0;
+  const int32_t* seq_len;  // nullptr in prefill
+  int32_t* idx;
+  int32_t* cnt;
+  int kB, r, R;
+  double log2_theta;
+};
+
+size_t index_prefill_workspace(int B, int n_q, int num_cu, int kB);
+hipError_t launch_index_prefill(qsa_dtype dt, const IndexArgs& a, void* ws, int num_cu,
+                                hipStream_t st);
+size_t index_decode_workspace(int B, int n_q, int64_t nb_cap);
+hipError_t launch_index_decode(qsa_dtype dt, const IndexArgs& a, void* ws, hipStream_t st);
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  const int32_t* idx;
+  const int32_t* cnt;
+  const int32_t* seq_len;  // nullptr in prefill
+  int64_t n_cap;
+  int64_t q_pos0;
+  int B, n_q, hq, hkv, kB, r;
+  float scale;
+};
+
+hipError_t launch_attn_prefill(qsa_dtype dt, const AttnArgs& a, hipStream_t st);
+size_t attn_decode_workspace(int B, int n_q, int hkv, int kB);
+hipError_t launch_attn_decode(qsa_dtype dt, const AttnArgs& a, void* ws, hipStream_t st);
+
+}  // namespace qsa
