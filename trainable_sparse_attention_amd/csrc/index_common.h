@@ -25,6 +25,14 @@ __device__ __forceinline__ float relu_sum4(const f32x4& acc) {
   return __uint_as_float(__float_as_uint(s) & 0x7fffffffu);
 }
 
+// q = hi + lo with hi = bf16(q) and lo = bf16(q - hi): the pair carries
+// 16 significant bits, so a rotated query keeps float-level accuracy in the
+// bf16 contraction (bf16 x bf16 products are exact in the fp32 accumulator).
+__device__ __forceinline__ void split_bf16(float v, unsigned short* hi, unsigned short* lo) {
+  *hi = f32_to_bf16(v);
+  *lo = f32_to_bf16(v - bf16_to_f32(*hi));
+}
+
 // Score contraction traits.  A 16x16 output tile holds 4 queries x 4 heads
 // (rows) by 16 blocks (columns); lane (hl = lane%16, g = lane/16) receives
 // the 4 heads of query g for block hl.
@@ -32,10 +40,13 @@ __device__ __forceinline__ float relu_sum4(const f32x4& acc) {
 //         call c = dims 32c + 8g .. 32c + 8g + 7.
 //   fp32: v_mfma_f32_16x16x4f32, 32 calls; lane operand of call c = dim
 //         32g + c.
+// NLO: number of leading 32-dim steps that hold rotated dims (ceil(R/32)),
+// the only steps whose bf16 query operand needs a low part.
 template <typename T> struct Mma;
 
 template <> struct Mma<unsigned short> {
   static constexpr int kCalls = 4;
+  static constexpr bool kSplit = true;  // rotated query dims carry a bf16 low part
   typedef bf16x8 Frag;
   // Fragment of row `row` (16 rows stored [16][ld] in LDS, bf16).
   __device__ __forceinline__ static void load_lds(const unsigned short* base, int ld_elems,
@@ -49,16 +60,23 @@ template <> struct Mma<unsigned short> {
     for (int c = 0; c < 4; ++c)
       f[c] = __builtin_bit_cast(bf16x8, *(const u16x8*)(row_ptr + 32 * c + 8 * g));
   }
-  __device__ __forceinline__ static f32x4 dot(const Frag* a, const Frag* b) {
+  // <a_hi + a_lo, b>: a_lo is non-zero only in the first NLO 32-dim steps
+  // (the rotated dims), so only those steps are issued twice.
+  template <int NLO>
+  __device__ __forceinline__ static f32x4 dot(const Frag* a, const Frag* alo, const Frag* b) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c], b[c], acc, 0, 0, 0);
+    for (int c = 0; c < 4; ++c) {
+      if (c < NLO) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[c], b[c], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c], b[c], acc, 0, 0, 0);
+    }
     return acc;
   }
 };
 
 template <> struct Mma<float> {
   static constexpr int kCalls = 32;
+  static constexpr bool kSplit = false;
   typedef float Frag;
   __device__ __forceinline__ static void load_lds(const float* base, int ld_elems, int row, int g,
                                                   Frag* f) {
@@ -81,7 +99,8 @@ template <> struct Mma<float> {
       f[4 * e + 3] = v[3];
     }
   }
-  __device__ __forceinline__ static f32x4 dot(const Frag* a, const Frag* b) {
+  template <int NLO>
+  __device__ __forceinline__ static f32x4 dot(const Frag* a, const Frag* /*alo*/, const Frag* b) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 32; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[c], b[c], acc, 0, 0, 0);

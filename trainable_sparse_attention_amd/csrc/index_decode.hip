@@ -62,7 +62,7 @@ static DecodeWs carve(void* ws, int B, int n_q, int64_t nb_cap) {
   return d;
 }
 
-template <typename T>
+template <typename T, int NLO>
 __global__ __launch_bounds__(kScanThreads) void index_decode_scan(IndexArgs a, DecodeWs w) {
   typedef Mma<T> M;
   __shared__ uint32_t hist[4][kBins];
@@ -86,9 +86,13 @@ __global__ __launch_bounds__(kScanThreads) void index_decode_scan(IndexArgs a, D
     table[t][j] = make_float2(c, s);
   }
   __syncthreads();
-  // rotated query rows 4t + h (t < n_q), rows of absent tokens are zero
+  // rotated query rows 4t + h (t < n_q), rows of absent tokens are zero;
+  // bf16 keeps a low part for the rotated dims (see split_bf16)
   const T* qsrc = (const T*)a.q_idx;
-  for (int e = tid; e < 16 * 128; e += kScanThreads) {
+  float vals[16 * 128 / kScanThreads];
+#pragma unroll
+  for (int u = 0; u < 16 * 128 / kScanThreads; ++u) {
+    const int e = tid + kScanThreads * u;
     const int rr = e >> 7, d = e & 127, t = rr >> 2, hh = rr & 3;
     float val = 0.f;
     if (t < a.n_q) {
@@ -103,11 +107,21 @@ __global__ __launch_bounds__(kScanThreads) void index_decode_scan(IndexArgs a, D
         val = x;
       }
     }
+    vals[u] = val;
     Elt<T>::st(qrot, e, val);
   }
   __syncthreads();
   typename M::Frag A[M::kCalls];
+  typename M::Frag Alo[M::kSplit ? M::kCalls : 1];
   M::load_lds(qrot, 128, hl, gq, A);
+  if constexpr (M::kSplit && NLO > 0) {
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 16 * 128 / kScanThreads; ++u)
+      Elt<T>::st(qrot, tid + kScanThreads * u, vals[u] - bf16_to_f32(f32_to_bf16(vals[u])));
+    __syncthreads();
+    M::load_lds(qrot, 128, hl, gq, Alo);
+  }
 
   const int64_t nbmax = nbt[a.n_q - 1];
   const int64_t lo = (int64_t)split * w.chunk;
@@ -124,7 +138,7 @@ __global__ __launch_bounds__(kScanThreads) void index_decode_scan(IndexArgs a, D
     const bool has1 = c1 < hi;
     if (has1) M::load_glb(kb + r1 * 128, gq, B1);
     {
-      const float sc = relu_sum4(M::dot(A, B0));
+      const float sc = relu_sum4(M::template dot<NLO>(A, Alo, B0));
       const int64_t blk = c0 + hl;
       if (blk < hi && blk < my_nb) {
         srow[blk] = sc;
@@ -132,7 +146,7 @@ __global__ __launch_bounds__(kScanThreads) void index_decode_scan(IndexArgs a, D
       }
     }
     if (has1) {
-      const float sc = relu_sum4(M::dot(A, B1));
+      const float sc = relu_sum4(M::template dot<NLO>(A, Alo, B1));
       const int64_t blk = c1 + hl;
       if (blk < hi && blk < my_nb) {
         srow[blk] = sc;
@@ -312,10 +326,14 @@ hipError_t launch_index_decode(qsa_dtype dt, const IndexArgs& a, void* ws, hipSt
   if (a.B == 0) return hipSuccess;
   const DecodeWs w = carve(ws, a.B, a.n_q, a.nb_cap);
   const dim3 g1((unsigned)w.nsplit, (unsigned)a.B);
-  if (dt == QSA_BF16)
-    hipLaunchKernelGGL(index_decode_scan<unsigned short>, g1, dim3(kScanThreads), 0, st, a, w);
+  if (dt != QSA_BF16)
+    hipLaunchKernelGGL((index_decode_scan<float, 0>), g1, dim3(kScanThreads), 0, st, a, w);
+  else if (a.R == 0)
+    hipLaunchKernelGGL((index_decode_scan<unsigned short, 0>), g1, dim3(kScanThreads), 0, st, a, w);
+  else if (a.R <= 64)
+    hipLaunchKernelGGL((index_decode_scan<unsigned short, 2>), g1, dim3(kScanThreads), 0, st, a, w);
   else
-    hipLaunchKernelGGL(index_decode_scan<float>, g1, dim3(kScanThreads), 0, st, a, w);
+    hipLaunchKernelGGL((index_decode_scan<unsigned short, 4>), g1, dim3(kScanThreads), 0, st, a, w);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(index_decode_select, dim3((unsigned)(a.B * a.n_q)), dim3(kSelThreads), 0, st,

@@ -37,7 +37,21 @@ template <typename T> struct PrefillLds {
 
 }  // namespace
 
-template <typename T>
+// Wave-wide cut of one candidate list (see wave_radix_kth / wave_keep_topk).
+// mode 0: keep the top k in place and return the new threshold (just above
+// the k-th score); mode 1: write the ascending ids of the top k to `out`.
+__device__ __forceinline__ float cut_list(uint64_t* lb, int c, int k, uint32_t* hist, int lane,
+                                       int mode, int32_t* out, int kB) {
+  __threadfence();
+  uint32_t v;
+  int krem;
+  wave_radix_kth(lb, c, k, hist, lane, &v, &krem);
+  wave_keep_topk(lb, c, k, v, krem, lane, mode, out, kB);
+  __threadfence();
+  return __uint_as_float(v + 1u);
+}
+
+template <typename T, int NLO>
 __global__ __launch_bounds__(512, 1) void index_prefill_kernel(IndexArgs a, uint64_t* cand_all,
                                                                int cap, int ntiles, int total,
                                                                int region_a_bytes) {
@@ -49,10 +63,13 @@ __global__ __launch_bounds__(512, 1) void index_prefill_kernel(IndexArgs a, uint
   const int half = a.R / 2;
   // Region A: prologue (rope table + rotated-query scratch) then the stages.
   float2* table = (float2*)smem;                                         // [128][half]
-  T* scratch = (T*)(smem + (size_t)kRows * (half > 0 ? half : 1) * sizeof(float2));
+  float* scratch = (float*)(smem + (size_t)kRows * (half > 0 ? half : 1) * sizeof(float2));
   T* stage0 = (T*)smem;
   T* stage1 = (T*)(smem + LDS::kStageBytes);
   uint32_t* hist = (uint32_t*)(smem + region_a_bytes) + wv * 256;
+  // per-wave query state while a list is cut: [16] counts, [16] thresholds
+  int* qcnt = (int*)(smem + region_a_bytes + kWaves * 256 * 4) + wv * 32;
+  float* qtau = (float*)(qcnt + 16);
   uint64_t* cand_wg = cand_all + (size_t)blockIdx.x * kRows * cap;
 
   for (int L = blockIdx.x; L < total; L += gridDim.x) {
@@ -72,13 +89,14 @@ __global__ __launch_bounds__(512, 1) void index_prefill_kernel(IndexArgs a, uint
     }
     __syncthreads();
     typename M::Frag A[4][M::kCalls];
+    typename M::Frag Alo[4][(M::kSplit && NLO > 0) ? NLO : 1];
     int nbq[4];
     {
-      T* scr = scratch + wv * LDS::kScratchElems;
+      float* scr = scratch + wv * LDS::kScratchElems;
       const T* qsrc = (const T*)a.q_idx;
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        // rows of this row tile: 4 queries (16 wv + 4 rt + x) x 4 heads
+        // rows of this row tile: 4 queries (16 wv + 4 rt + x) x 4 heads, in float
         for (int e = lane; e < 16 * 128; e += 64) {
           const int rr = e >> 7, d = e & 127;
           const int ql = 16 * wv + 4 * rt + (rr >> 2), hh = rr & 3;
@@ -96,10 +114,32 @@ __global__ __launch_bounds__(512, 1) void index_prefill_kernel(IndexArgs a, uint
               val = x;
             }
           }
-          Elt<T>::st(scr, e, val);
+          scr[e] = val;
         }
         wave_sync();
-        M::load_lds(scr, 128, hl, gq, A[rt]);
+        if constexpr (M::kSplit) {
+          // bf16 fragment of row hl, call c: dims 32c + 8gq .. +7 (hi and lo)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const f32x4 v0 = *(const f32x4*)(scr + hl * 128 + 32 * c + 8 * gq);
+            const f32x4 v1 = *(const f32x4*)(scr + hl * 128 + 32 * c + 8 * gq + 4);
+            u16x8 hi, lo;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float v = j < 4 ? v0[j] : v1[j - 4];
+              unsigned short h16, l16;
+              split_bf16(v, &h16, &l16);
+              hi[j] = h16;
+              lo[j] = l16;
+            }
+            A[rt][c] = __builtin_bit_cast(typename M::Frag, hi);
+            if constexpr (NLO > 0) {
+              if (c < NLO) Alo[rt][c < NLO ? c : 0] = __builtin_bit_cast(typename M::Frag, lo);
+            }
+          }
+        } else {
+          M::load_lds((const T*)scr, 128, hl, gq, A[rt]);
+        }
         wave_sync();
         const int t = row0 + 16 * wv + 4 * rt + gq;
         nbq[rt] = t < a.n_q ? (int)((seq_off + t + 1) / a.r) : 0;
@@ -148,7 +188,7 @@ __global__ __launch_bounds__(512, 1) void index_prefill_kernel(IndexArgs a, uint
         const int blk = col0 + hl;
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-          const f32x4 acc = M::dot(A[rt], Bf);
+          const f32x4 acc = M::template dot<NLO>(A[rt], Alo[rt], Bf);
           const float sc = relu_sum4(acc);
           const bool pass = (blk < nbq[rt]) && (sc >= tau[rt]);
           const uint64_t bal = __ballot(pass);
@@ -169,51 +209,57 @@ __global__ __launch_bounds__(512, 1) void index_prefill_kernel(IndexArgs a, uint
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) full |= cnt[rt] > cap - kStageBlk;
       if (__ballot(full)) {
-        __threadfence();
+        if (hl == 0) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          for (int x = 0; x < 4; ++x) {
-            const int c = __shfl(cnt[rt], 16 * x);
-            if (c > cap - kStageBlk) {
-              uint64_t* lb = mybuf + (size_t)(4 * rt + x) * cap;
-              uint32_t v;
-              int krem;
-              wave_radix_kth(lb, c, a.kB, hist, lane, &v, &krem);
-              wave_keep_topk(lb, c, a.kB, v, krem, lane, 0, nullptr, 0);
-              __threadfence();
-              if (gq == x) {
-                cnt[rt] = a.kB;
-                tau[rt] = __uint_as_float(v + 1u);  // strictly above the k_B-th score
-              }
-            }
+          for (int rt = 0; rt < 4; ++rt) {
+            qcnt[4 * rt + gq] = cnt[rt];
+            qtau[4 * rt + gq] = tau[rt];
           }
         }
+        wave_sync();
+        for (int q = 0; q < 16; ++q) {
+          const int c = qcnt[q];
+          if (c > cap - kStageBlk) {
+            const float nt = cut_list(mybuf + (size_t)q * cap, c, a.kB, hist, lane, 0, nullptr, 0);
+            wave_sync();
+            if (lane == 0) {
+              qcnt[q] = a.kB;
+              qtau[q] = nt;
+            }
+            wave_sync();
+          }
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          cnt[rt] = qcnt[4 * rt + gq];
+          tau[rt] = qtau[4 * rt + gq];
+        }
+        wave_sync();
       }
       __syncthreads();
     }
 
     // ---- final selection: exact top-min(k_B, visible), ascending ids ------
-    __threadfence();
+    if (hl == 0) {
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      for (int x = 0; x < 4; ++x) {
-        const int t = row0 + 16 * wv + 4 * rt + x;
-        if (t >= a.n_q) continue;
-        const int c = __shfl(cnt[rt], 16 * x);
-        const int nb = __shfl(nbq[rt], 16 * x);
-        const int k = min(a.kB, nb);
-        int32_t* out = a.idx + ((int64_t)b * a.n_q + t) * a.kB;
-        uint64_t* lb = mybuf + (size_t)(4 * rt + x) * cap;
-        if (k == 0) {
-          for (int e = lane; e < a.kB; e += 64) out[e] = -1;
-        } else {
-          uint32_t v;
-          int krem;
-          wave_radix_kth(lb, c, k, hist, lane, &v, &krem);
-          wave_keep_topk(lb, c, k, v, krem, lane, 1, out, a.kB);
-        }
-        if (lane == 0) a.cnt[(int64_t)b * a.n_q + t] = k;
+      for (int rt = 0; rt < 4; ++rt) {
+        qcnt[4 * rt + gq] = cnt[rt];
+        qcnt[16 + 4 * rt + gq] = nbq[rt];  // reuses the threshold slots
       }
+    }
+    wave_sync();
+    for (int q = 0; q < 16; ++q) {
+      const int t = row0 + 16 * wv + q;
+      if (t >= a.n_q) break;
+      const int c = qcnt[q];
+      const int k = min(min(a.kB, qcnt[16 + q]), c);
+      int32_t* out = a.idx + ((int64_t)b * a.n_q + t) * a.kB;
+      if (k == 0) {
+        for (int e = lane; e < a.kB; e += 64) out[e] = -1;
+      } else {
+        cut_list(mybuf + (size_t)q * cap, c, k, hist, lane, 1, out, a.kB);
+      }
+      if (lane == 0) a.cnt[(int64_t)b * a.n_q + t] = k;
     }
     __syncthreads();
   }
@@ -238,32 +284,34 @@ size_t index_prefill_workspace(int B, int n_q, int num_cu, int kB) {
 template <typename T> static int region_a_bytes(int R) {
   typedef PrefillLds<T> LDS;
   const int half = R / 2 > 0 ? R / 2 : 1;
-  const int pro = kRows * half * (int)sizeof(float2) + kWaves * LDS::kScratchElems * (int)sizeof(T);
+  const int pro = kRows * half * (int)sizeof(float2) + kWaves * LDS::kScratchElems * 4;
   const int stg = 2 * LDS::kStageBytes;
   const int r = pro > stg ? pro : stg;
   return (r + 15) & ~15;
 }
 
-template <typename T>
+template <typename T, int NLO>
 static hipError_t launch_t(const IndexArgs& a, void* ws, int num_cu, hipStream_t st) {
   const int ntiles = (a.n_q + kRows - 1) / kRows;
   const int total = ntiles * a.B;
   const int grid = prefill_grid(a.B, a.n_q, num_cu);
   const int ra = region_a_bytes<T>(a.R);
-  const int lds = ra + kWaves * 256 * 4;
-  hipError_t e = hipFuncSetAttribute((const void*)index_prefill_kernel<T>,
+  const int lds = ra + kWaves * 256 * 4 + kWaves * 32 * 4;
+  hipError_t e = hipFuncSetAttribute((const void*)index_prefill_kernel<T, NLO>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(index_prefill_kernel<T>, dim3(grid), dim3(512), lds, st, a, (uint64_t*)ws,
-                     prefill_cap(a.kB), ntiles, total, ra);
+  hipLaunchKernelGGL((index_prefill_kernel<T, NLO>), dim3(grid), dim3(512), lds, st, a,
+                     (uint64_t*)ws, prefill_cap(a.kB), ntiles, total, ra);
   return hipGetLastError();
 }
 
 hipError_t launch_index_prefill(qsa_dtype dt, const IndexArgs& a, void* ws, int num_cu,
                                 hipStream_t st) {
   if (a.n_q == 0 || a.B == 0) return hipSuccess;
-  return dt == QSA_BF16 ? launch_t<unsigned short>(a, ws, num_cu, st)
-                        : launch_t<float>(a, ws, num_cu, st);
+  if (dt != QSA_BF16) return launch_t<float, 0>(a, ws, num_cu, st);
+  if (a.R == 0) return launch_t<unsigned short, 0>(a, ws, num_cu, st);
+  if (a.R <= 64) return launch_t<unsigned short, 2>(a, ws, num_cu, st);
+  return launch_t<unsigned short, 4>(a, ws, num_cu, st);
 }
 
 }  // namespace qsa

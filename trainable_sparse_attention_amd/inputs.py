@@ -12,11 +12,13 @@ then rounded round-to-nearest-even to the storage type.  The draw order is
 q_idx, k_idx, q, k, v, then the planting draws.
 
 Planting: a planted match pairs a query row i with a block b it can see
-(only rows that see more than k_B blocks).  Every token of block b gets
-k_idx = c * q_idx[i, h] for a random indexer head h, and, in the attention
-KV head g of a random query head a, k[g, token] = 4 c * q[i, a]; c is drawn
-uniform in [2, 4] (config 0 uses c = 4 exactly).  Decode configurations
-plant against the one new query of each sequence.
+(only rows that see more than k_B blocks).  Every token of block b gets, on
+the indexer dims that are not position-rotated (64..127), k_idx = c *
+q_idx[i, h] for a random indexer head h, and zeros on the rotated dims
+(0..63), so the match does not depend on the distance between i and b; in
+the attention KV head g of a random query head a, k[g, token] = 4 c *
+q[i, a].  c is drawn uniform in [2, 4] (config 0 uses c = 4 exactly).
+Decode configurations plant against the one new query of each sequence.
 
 Two generators exist: ``numpy`` (Philox on the host; used by the CPU tests
 and the small GPU parity cases) and ``torch`` (Philox on the GPU through
@@ -114,7 +116,9 @@ def make(cfg="cfg0", seed=0, backend="numpy", device="cuda", overrides=None):
                 qi = 0 if mode == "decode" else i
                 g = (a * hkv) // hq
                 for tok in range(blk * r, blk * r + r):
-                    arrs["k_idx"][b, tok, :] = np.float32(c) * arrs["q_idx"][b, qi, h, :]
+                    arrs["k_idx"][b, tok, :ROPE_DIMS] = 0.0
+                    arrs["k_idx"][b, tok, ROPE_DIMS:] = np.float32(c) * \
+                        arrs["q_idx"][b, qi, h, ROPE_DIMS:]
                     arrs["k"][b, g, tok, :] = np.float32(4.0 * c) * arrs["q"][b, qi, a, :]
                 plants.append((b, i, blk, h, a, c))
         for name in arrs:
@@ -154,6 +158,7 @@ def make(cfg="cfg0", seed=0, backend="numpy", device="cuda", overrides=None):
                 qi = 0 if mode == "decode" else i
                 gk = (a * hkv) // hq
                 src_i = res["q_idx"][b, qi, h, :].float() * c
+                src_i[:ROPE_DIMS] = 0.0
                 src_a = res["q"][b, qi, a, :].float() * (4.0 * c)
                 res["k_idx"][b, blk * r:blk * r + r, :] = src_i.to(tdt)[None, :]
                 res["k"][b, gk, blk * r:blk * r + r, :] = src_a.to(tdt)[None, :]
