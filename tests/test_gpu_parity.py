@@ -313,3 +313,40 @@ def test_full_size_decode_sampled(cfg, check):
         err = rel_err(to_host(out[b]), o)
         say(cfg, "seq", b, "attention rel err", err)
         assert err <= TOL["bf16"]
+
+
+def test_threshold_fallback_rescan():
+    """White-box: rows that see more than 4032 blocks first estimate their
+    threshold from a strided sample of the blocks (the last tile of 128 rows
+    here samples m = 1024 blocks u * nbmin // m of the nbmin blocks its
+    first row sees).  Planting high scores exactly on those blocks for the
+    last row makes the estimate too high, so that row must be streamed again
+    exactly; the selection must still equal the oracle's."""
+    say("threshold fallback")
+    n = 20480
+    d = inputs.small(B=1, n=n, hq=4, hkv=1, dtype="bf16", seed=77)
+    i = n - 1
+    row0 = (n - 1) // 128 * 128
+    nbmin = (row0 + 1) // 4
+    m = max(1024, min(2048, nbmin // 16))
+    sample = [u * nbmin // m for u in range(m)]
+    planted = sample[::5][:200]  # distinct high scores on 200 sampled blocks
+    qf = inputs.bf16_bits_to_f32(d["q_idx"][0, i, 0])
+    kf = inputs.bf16_bits_to_f32(d["k_idx"][0])
+    for u, blk in enumerate(planted):
+        kf[4 * blk:4 * blk + 4, :64] = 0.0
+        kf[4 * blk:4 * blk + 4, 64:] = (3.0 + 0.01 * u) * qf[64:]
+    d["k_idx"][0] = inputs.f32_to_bf16_bits(kf)
+    p = _params()
+    t = _dev_inputs(d)
+    kbar = _pool_gpu(p, t["k_idx"], n // 4)
+    idx, cnt = _index_gpu(p, t["q_idx"], kbar)
+    torch.cuda.synchronize()
+    kbar_h, g_idx, g_cnt = to_host(kbar), to_host(idx), to_host(cnt)
+    rows = np.arange(row0, n)
+    near, o_idx, _ = _check_index_rows(0, rows, g_idx, g_cnt, d["q_idx"][0], kbar_h[0], 2048)
+    # the threshold estimate (the j-th largest sample score, j < 200) left
+    # fewer than k_B candidates: the rescan must recover all planted blocks
+    # plus the best noise blocks
+    assert set(planted) <= set(g_idx[0, i, :g_cnt[0, i]].tolist())
+    assert g_cnt[0, i] == 512

@@ -316,7 +316,8 @@ __global__ __launch_bounds__(kSelThreads) void index_decode_select(IndexArgs a, 
   if (wv == 0) {
     uint32_t v;
     int krem;
-    wave_radix_kth(cand, c, (int)k, whist[0], lane, &v, &krem);
+    wave_radix_kth([&](int e) { return (uint32_t)(cand[e] >> 32); }, c, (int)k, whist[0], lane,
+                   &v, &krem);
     wave_keep_topk(cand, c, (int)k, v, krem, lane, 1, out, a.kB);
     if (lane == 0) a.cnt[(int64_t)b * a.n_q + t] = (int)k;
   }
