@@ -144,9 +144,11 @@ def test_small_and_ragged(n, dtype, K):
         assert rel_err(g_out[b], o) <= TOL[dtype]
 
 
-def test_large_K_is_dense():
-    say("K >= n: dense causal")
-    n = 600
+@pytest.mark.parametrize("n", [600, 3000])
+def test_large_K_is_dense(n):
+    # n = 3000 gives rows with up to 751 slots, more than one LDS window of
+    # slot ids in the bf16 attention kernel
+    say("K >= n: dense causal, n=%d" % n)
     d = inputs.small(B=1, n=n, hq=16, hkv=2, dtype="bf16", K=4096, seed=5)
     p = _params(K=4096)
     t = _dev_inputs(d)

@@ -27,6 +27,7 @@ namespace {
 
 constexpr int kSlotsPerChunk = 8;
 constexpr int kVRow = 128 + 8;  // LDS row of V in bf16 elements (16 B pad)
+constexpr int kIdWin = 576;     // slot ids staged in LDS at a time (whole chunks)
 
 struct Row {
   int64_t pos;
@@ -92,8 +93,18 @@ __device__ __forceinline__ void decode_job(const AttnArgs& a, int nsplit, int* b
 // part layout per (b, t, g, split): m[16], l[16], o[16][128] floats.
 constexpr int kPartFloats = 16 + 16 + 16 * 128;
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// V chunk layout in LDS: key row kk (256 bytes) keeps its 16-byte chunk c at
+// chunk c ^ (4 * ((kk >> 2) & 3)), so that the transposed reads of the four
+// lane groups (keys 4 g + j) fall in different banks.
+__device__ __forceinline__ int vswz(int kk, int c) { return c ^ (((kk >> 2) & 3) << 2); }
+
 __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, float* part) {
-  __shared__ __attribute__((aligned(16))) unsigned short vs[32 * kVRow];
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_attn[];
+  unsigned short* vbuf = (unsigned short*)smem_attn;      // [2][32 keys][128]
+  int* ids = (int*)(smem_attn + 2 * 32 * 128 * 2);          // block of each slot
   const int lane = threadIdx.x;
   const int hl = lane & 15, gq = lane >> 4;
   int b, t, g, split;
@@ -104,9 +115,23 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
     s0 = split * kSlotsPerChunk;
     s1 = min(R.nslots, s0 + kSlotsPerChunk);
   }
+  // Block ids of a window of kIdWin slots from `base` (the tail slot is block
+  // nb; slots past the set read block 0 and are masked).
+  int base = s0;
+  auto fill_ids = [&](int b0) {
+    for (int u = lane; u < kIdWin; u += 64) {
+      const int sl = b0 + u;
+      ids[u] = sl < R.cnt ? R.ids[sl] : (sl < s1 ? (int)R.nb : 0);
+    }
+  };
+  fill_ids(base);
+  __syncthreads();
+  auto row_of = [&](int u, int tok) -> int64_t {  // token row of key tok of slot u, 0 if absent
+    const bool ok = u < s1 && (u < R.cnt || tok < R.ntail);
+    return ok ? (int64_t)ids[u - base] * a.r + tok : 0;
+  };
   const int G = a.hq / a.hkv;
   const int head = g * G + hl;
-  const unsigned short* qs = (const unsigned short*)a.q;
   const unsigned short* ks =
       (const unsigned short*)a.k + ((int64_t)b * a.hkv + g) * a.n_cap * 128;
   const unsigned short* vsrc =
@@ -114,7 +139,8 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
 
   bf16x8 qf[4];
   {
-    const unsigned short* qrow = qs + (((int64_t)b * a.n_q + t) * a.hq + head) * 128;
+    const unsigned short* qrow =
+        (const unsigned short*)a.q + (((int64_t)b * a.n_q + t) * a.hq + head) * 128;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
       u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -122,33 +148,51 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
       qf[cc] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  // K operands of a chunk: key row hl of tile kt = slot s + 4kt + hl/4,
+  // token hl%4, dims 32cc + 8gq.
+  auto load_k = [&](int s, bf16x8 (*kf)[4]) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const unsigned short* kr = ks + row_of(s + 4 * kt + (hl >> 2), hl & 3) * 128 + 8 * gq;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+        kf[kt][cc] = __builtin_bit_cast(bf16x8, *(const u16x8*)(kr + 32 * cc));
+    }
+  };
+  // V of a chunk straight into LDS: instruction i moves slot s + i (1 KB);
+  // lane l's 16 bytes land at key 4i + l/16, chunk l%16 of that key row.
+  auto load_v = [&](int s, unsigned short* dst) {
+#pragma unroll
+    for (int i = 0; i < kSlotsPerChunk; ++i) {
+      const int kk = 4 * i + (lane >> 4);
+      const int c = vswz(kk, lane & 15);  // logical chunk stored at this lane's position
+      const unsigned short* src = vsrc + row_of(s + i, lane >> 4) * 128 + 8 * c;
+      __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)(dst + i * 512), 16, 0,
+                                       0);
+    }
+  };
+
   const float sl2 = a.scale * 1.4426950408889634f;
   f32x4 o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
 
-  for (int s = s0; s < s1; s += kSlotsPerChunk) {
-    // K fragments: key row hl of tile kt = slot s + 4kt + hl/4, token hl%4.
-    bf16x8 kf[2][4];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      int64_t row;
-      slot_row(R, s + 4 * kt + (hl >> 2), s1, hl & 3, a.r, &row);
-      const unsigned short* kr = ks + row * 128 + 8 * gq;
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
-        kf[kt][cc] = __builtin_bit_cast(bf16x8, *(const u16x8*)(kr + 32 * cc));
-    }
-    // V chunk to LDS: lane -> key lane/2 (slot s + key/4), half lane%2.
-    {
-      const int kk = lane >> 1;
-      int64_t row;
-      slot_row(R, s + (kk >> 2), s1, kk & 3, a.r, &row);
-      const unsigned short* vr = vsrc + row * 128 + 64 * (lane & 1);
-      unsigned short* dst = vs + kk * kVRow + 64 * (lane & 1);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) *(u16x8*)(dst + 8 * e) = *(const u16x8*)(vr + 8 * e);
+  bf16x8 kcur[2][4], knext[2][4];
+  if (s0 < s1) {
+    load_k(s0, kcur);
+    load_v(s0, vbuf);
+  }
+  int buf = 0;
+  for (int s = s0; s < s1; s += kSlotsPerChunk, buf ^= 1) {
+    const bool more = s + kSlotsPerChunk < s1;
+    if (more) {  // prefetch the next chunk while this one is computed
+      if (s + kSlotsPerChunk - base >= kIdWin) {
+        base = s + kSlotsPerChunk;
+        fill_ids(base);
+      }
+      load_k(s + kSlotsPerChunk, knext);
+      load_v(s + kSlotsPerChunk, vbuf + (buf ^ 1) * 32 * 128);
     }
     // S^T tiles: lane holds head hl, keys 16kt + 4gq + i.
     f32x4 sacc[2];
@@ -157,18 +201,18 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
       sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc)
-        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt][cc], qf[cc], sacc[kt], 0, 0, 0);
+        sacc[kt] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(kcur[kt][cc], qf[cc], sacc[kt], 0, 0, 0);
     }
     float sv[8];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int u = s + 4 * kt + gq;
+      const bool slot_ok = u < s1;
+      const int ntok = u < R.cnt ? a.r : R.ntail;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int64_t row;
-        const bool ok = slot_row(R, u, s1, i, a.r, &row);
-        sv[4 * kt + i] = ok ? sacc[kt][i] * sl2 : -INFINITY;
-      }
+      for (int i = 0; i < 4; ++i)
+        sv[4 * kt + i] = (slot_ok && i < ntok) ? sacc[kt][i] * sl2 : -INFINITY;
     }
     float mx = sv[0];
 #pragma unroll
@@ -189,22 +233,35 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
 #pragma unroll
     for (int j = 0; j < 8; ++j) pb[j] = f32_to_bf16(p[j]);
     const bf16x8 pf = __builtin_bit_cast(bf16x8, pb);
+    // this chunk's V has landed once at most the next chunk's loads are pending
+    if (more)
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    // O^T tile tt: rows dims 16tt + (A row), B = P^T; A row = dim 16tt + hl,
-    // k index 8gq + j <-> key (j < 4 ? 4gq + j : 16 + 4gq + j - 4).
+    const unsigned short* vs = vbuf + buf * 32 * 128;
+    // O^T tile tt: A row = dim 16tt + hl, k index 8gq + j <-> key
+    // (j < 4 ? 4gq + j : 16 + 4gq + j - 4); B = P^T.
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
       u16x8 vv;
+      const int c = 2 * tt + (hl >> 3);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int kk = (j < 4) ? (4 * gq + j) : (16 + 4 * gq + j - 4);
-        vv[j] = vs[kk * kVRow + 16 * tt + hl];
+        vv[j] = vs[kk * 128 + vswz(kk, c) * 8 + (hl & 7)];
       }
       o[tt] = o[tt] * alpha;
       o[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, o[tt],
                                                       0, 0, 0);
     }
-    __syncthreads();
+    __syncthreads();  // all reads of this buffer done before it is refilled
+    if (more) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) kcur[kt][cc] = knext[kt][cc];
+    }
   }
 
   if (nsplit == 1) {
@@ -397,14 +454,17 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, int nspli
   Elt<T>::st((T*)a.out, (((int64_t)b * a.n_q + t) * a.hq + h) * 128 + dim, acc / L);
 }
 
+// LDS of the bf16 kernel: two V chunks and a window of slot ids.
+static size_t bf16_lds_bytes() { return 2 * 32 * 128 * 2 + (size_t)kIdWin * 4; }
+
 static int decode_splits(int kB) { return (kB + 1 + kSlotsPerChunk - 1) / kSlotsPerChunk; }
 
 hipError_t launch_attn_prefill(qsa_dtype dt, const AttnArgs& a, hipStream_t st) {
   const int64_t waves = (int64_t)a.B * a.n_q * a.hkv;
   if (waves == 0) return hipSuccess;
   if (dt == QSA_BF16)
-    hipLaunchKernelGGL(attn_bf16_kernel, dim3((unsigned)waves), dim3(64), 0, st, a, 1,
-                       (float*)nullptr);
+    hipLaunchKernelGGL(attn_bf16_kernel, dim3((unsigned)waves), dim3(64), bf16_lds_bytes(), st,
+                       a, 1, (float*)nullptr);
   else
     hipLaunchKernelGGL(attn_f32_kernel, dim3((unsigned)waves), dim3(64), 0, st, a, 1,
                        (float*)nullptr);
@@ -421,7 +481,8 @@ hipError_t launch_attn_decode(qsa_dtype dt, const AttnArgs& a, void* ws, hipStre
   if (waves == 0) return hipSuccess;
   float* part = (float*)ws;
   if (dt == QSA_BF16)
-    hipLaunchKernelGGL(attn_bf16_kernel, dim3((unsigned)waves), dim3(64), 0, st, a, nsplit, part);
+    hipLaunchKernelGGL(attn_bf16_kernel, dim3((unsigned)waves), dim3(64), bf16_lds_bytes(), st,
+                       a, nsplit, part);
   else
     hipLaunchKernelGGL(attn_f32_kernel, dim3((unsigned)waves), dim3(64), 0, st, a, nsplit, part);
   hipError_t e = hipGetLastError();
