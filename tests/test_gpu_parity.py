@@ -238,6 +238,39 @@ def test_decode_parity(n_q, dtype):
         assert rel_err(g_out[b], o) <= TOL[dtype]
 
 
+def test_decode_exact_route_on_ties():
+    """Decode rows whose scores tie in bulk: sequence 0 has a zero indexer
+    query (every score is +0), sequence 1 a pooled cache whose keys are all
+    equal and unrotated (one score everywhere).  Far more blocks than fit the
+    candidate list share the k_B-th score, so the selection takes the exact
+    route; ties go to the smaller block id.  Sequence 2 is ordinary."""
+    say("decode exact route on ties")
+    L = 30000  # 7500 blocks
+    d = inputs.small(B=3, n=L, hq=16, hkv=2, dtype="bf16", seed=91)
+    d["q_idx"][0, L - 1] = 0
+    # every key = head 0's query on the unrotated dims, zero on the rotated
+    # ones: all pooled keys are equal and score the same positive value
+    d["k_idx"][1, :, :64] = 0
+    d["k_idx"][1, :, 64:] = d["q_idx"][1, L - 1, 0, 64:]
+    p = _params()
+    t = _dev_inputs(d)
+    nb = L // 4
+    kbar = _pool_gpu(p, t["k_idx"], nb)
+    seq_len = torch.full((3,), L, dtype=torch.int32, device="cuda")
+    qi = t["q_idx"][:, L - 1:L].contiguous()
+    idx, cnt = _index_gpu(p, qi, kbar, seq_len=seq_len)
+    torch.cuda.synchronize()
+    kbar_h, g_idx, g_cnt = to_host(kbar), to_host(idx), to_host(cnt)
+    for b in range(3):
+        o_idx, o_cnt = oracle.index_rows(d["q_idx"][b, L - 1:L], kbar_h[b], [0], L - 1)
+        if b < 2:
+            assert np.array_equal(o_idx[0], np.arange(512))
+            assert np.array_equal(g_idx[b], o_idx) and np.array_equal(g_cnt[b], o_cnt)
+        else:
+            sc = oracle.score_rows(d["q_idx"][b, L - 1:L], kbar_h[b], [0], L - 1)
+            check_sets(g_idx[b], g_cnt[b], o_idx, o_cnt, sc)
+
+
 # ---- full-size configurations, sampled rows --------------------------------
 
 def _sample_rows(n, plants, seed=0, nrand=96):

@@ -427,11 +427,15 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, int nsplit, fl
   }
 }
 
-// Merge split partials: one 128-thread block per (b, t, query head).
+// Merge split partials: one 128-thread block per (b, t, query head), thread =
+// output dim.  The split weights 2^(m_s - M) are formed once in LDS, then each
+// thread sums its dim over the splits with independent loads in flight.
 template <typename T>
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, int nsplit,
                                                            const float* __restrict__ part) {
-  const int dim = threadIdx.x;
+  extern __shared__ float wgt[];  // [nsplit]
+  __shared__ float red[2];
+  const int dim = threadIdx.x, lane = dim & 63, wv = dim >> 6;
   int64_t w = blockIdx.x;
   const int h = (int)(w % a.hq);
   w /= a.hq;
@@ -441,17 +445,36 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, int nspli
   const int g = h / G, hl = h % G;
   const float* base = part + (((int64_t)b * a.n_q + t) * a.hkv + g) * nsplit * kPartFloats;
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, base[(int64_t)s * kPartFloats + hl]);
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
+  for (int s = dim; s < nsplit; s += 128) M = fmaxf(M, base[(int64_t)s * kPartFloats + hl]);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) red[wv] = M;
+  __syncthreads();
+  M = fmaxf(red[0], red[1]);
+  float L = 0.f;
+  for (int s = dim; s < nsplit; s += 128) {
     const float* pp = base + (int64_t)s * kPartFloats;
     const float ms = pp[hl];
-    if (ms == -INFINITY) continue;
-    const float wgt = exp2f(ms - M);
-    L += pp[16 + hl] * wgt;
-    acc += pp[32 + hl * 128 + dim] * wgt;
+    const float ws = ms == -INFINITY ? 0.f : exp2f(ms - M);
+    wgt[s] = ws;
+    L += ws * pp[16 + hl];
   }
-  Elt<T>::st((T*)a.out, (((int64_t)b * a.n_q + t) * a.hq + h) * 128 + dim, acc / L);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) L += __shfl_xor(L, off);
+  __syncthreads();
+  if (lane == 0) red[wv] = L;
+  __syncthreads();
+  L = red[0] + red[1];
+  const float* po = base + 32 + hl * 128 + dim;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int s = 0;
+  for (; s + 8 <= nsplit; s += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += wgt[s + u] * po[(int64_t)(s + u) * kPartFloats];
+  }
+  for (; s < nsplit; ++s) acc[0] += wgt[s] * po[(int64_t)s * kPartFloats];
+  const float tot = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  Elt<T>::st((T*)a.out, (((int64_t)b * a.n_q + t) * a.hq + h) * 128 + dim, tot / L);
 }
 
 // LDS of the bf16 kernel: two V chunks and a window of slot ids.
@@ -489,11 +512,11 @@ hipError_t launch_attn_decode(qsa_dtype dt, const AttnArgs& a, void* ws, hipStre
   if (e != hipSuccess) return e;
   const dim3 cg((unsigned)((int64_t)a.B * a.n_q * a.hq));
   if (dt == QSA_BF16)
-    hipLaunchKernelGGL(attn_combine_kernel<unsigned short>, cg, dim3(128), 0, st, a, nsplit,
-                       (const float*)part);
+    hipLaunchKernelGGL(attn_combine_kernel<unsigned short>, cg, dim3(128), nsplit * sizeof(float),
+                       st, a, nsplit, (const float*)part);
   else
-    hipLaunchKernelGGL(attn_combine_kernel<float>, cg, dim3(128), 0, st, a, nsplit,
-                       (const float*)part);
+    hipLaunchKernelGGL(attn_combine_kernel<float>, cg, dim3(128), nsplit * sizeof(float), st, a,
+                       nsplit, (const float*)part);
   return hipGetLastError();
 }
 
