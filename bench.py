@@ -43,6 +43,10 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="uniformly spaced prefill rows the CPU oracle computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before timing, copy a buffer of MIB MiB with a plain device copy "
+                         "(3 times), so that a counter run can scale FETCH_SIZE / WRITE_SIZE "
+                         "by a kernel of known traffic")
     return ap.parse_args()
 
 
@@ -228,6 +232,17 @@ def main():
     from trainable_sparse_attention_amd import inputs, qsa
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     qsa.lib()
+    if args.copy_calibration > 0:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] copy calibration: %d bytes read and %d bytes written per copy" % (
+            nbytes, nbytes), file=sys.stderr, flush=True)
+        del src, dst
+        torch.cuda.empty_cache()
     pre, d = bench_prefill(args, torch, qsa, inputs)
     print("[bench] prefill %s: %.3f ms/step (pool %.3f, index %.3f, attn %.3f ms)" % (
         args.prefill_cfg, pre["ms"], *pre["stage_ms"]), file=sys.stderr, flush=True)

@@ -17,10 +17,13 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Wno-unused-function", "-Wno-unused-variable",
          # packed fp32 instructions are kept out of every kernel
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# per-file additions: the attention kernels keep MFMA accumulators in VGPRs,
+# where the online-softmax rescale can scale them without AGPR round trips
+EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src, obj):
-    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(HERE, "..", "include"), "-c",
+    cmd = [HIPCC] + FLAGS + EXTRA.get(src, []) + ["-I", os.path.join(HERE, "..", "include"), "-c",
                              os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()

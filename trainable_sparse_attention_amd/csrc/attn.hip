@@ -96,15 +96,35 @@ constexpr int kPartFloats = 16 + 16 + 16 * 128;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
-// V chunk layout in LDS: key row kk (256 bytes) keeps its 16-byte chunk c at
-// chunk c ^ (4 * ((kk >> 2) & 3)), so that the transposed reads of the four
-// lane groups (keys 4 g + j) fall in different banks.
-__device__ __forceinline__ int vswz(int kk, int c) { return c ^ (((kk >> 2) & 3) << 2); }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, float* part) {
+// V chunk layout in LDS: key row kk (256 bytes) keeps its 16-byte chunk c at
+// chunk c ^ 2(kk & 7), so that a transposed read (16 key rows x two
+// neighbouring chunks) touches every bank exactly twice.
+__device__ __forceinline__ int vswz(int kk, int c) { return c ^ ((kk & 7) << 1); }
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i%4
+// of the 8-byte rows addressed by lanes 4j + i/4 (j = 0..3), i.e. a 4 x 16
+// block of 16-bit values arrives transposed.
+__device__ __forceinline__ s16x4 lds_read_tr16(const unsigned short* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+}
+// LDS byte address of a pointer into workgroup memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
+}
+
+// WIN: the row's slots may exceed one LDS window of ids (refilled as the
+// scan advances); otherwise every slot id is staged once.
+template <bool WIN>
+__global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, float* part,
+                                                       int resident) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_attn[];
-  unsigned short* vbuf = (unsigned short*)smem_attn;      // [2][32 keys][128]
-  int* ids = (int*)(smem_attn + 2 * 32 * 128 * 2);          // block of each slot
+  unsigned short* vbuf = (unsigned short*)smem_attn;      // [32 keys][128]
+  int* ids = (int*)(smem_attn + 32 * 128 * 2);              // block of each slot
   const int lane = threadIdx.x;
   const int hl = lane & 15, gq = lane >> 4;
   int b, t, g, split;
@@ -126,16 +146,17 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
   };
   fill_ids(base);
   __syncthreads();
-  auto row_of = [&](int u, int tok) -> int64_t {  // token row of key tok of slot u, 0 if absent
+  // Token row of key tok of slot u with block id `id`, 0 if the key is not
+  // in T_i (branch-free).
+  auto row_sel = [&](int u, int id, int tok) -> uint32_t {
     const bool ok = u < s1 && (u < R.cnt || tok < R.ntail);
-    return ok ? (int64_t)ids[u - base] * a.r + tok : 0;
+    return ok ? (uint32_t)id * (uint32_t)a.r + (uint32_t)tok : 0u;
   };
   const int G = a.hq / a.hkv;
   const int head = g * G + hl;
-  const unsigned short* ks =
-      (const unsigned short*)a.k + ((int64_t)b * a.hkv + g) * a.n_cap * 128;
-  const unsigned short* vsrc =
-      (const unsigned short*)a.v + ((int64_t)b * a.hkv + g) * a.n_cap * 128;
+  // K/V rows of this (sequence, KV head); byte offsets within fit 32 bits
+  const char* kb = (const char*)a.k + ((int64_t)b * a.hkv + g) * a.n_cap * 256;
+  const char* vb = (const char*)a.v + ((int64_t)b * a.hkv + g) * a.n_cap * 256;
 
   bf16x8 qf[4];
   {
@@ -148,27 +169,40 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
       qf[cc] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  // The 8 block ids of the chunk at slot s (every slot of a loaded chunk
+  // lies in the window).  Read as two broadcast 16-byte LDS loads and kept
+  // in registers, so the address math needs no further LDS round trips.
+  auto chunk_ids = [&](int s, int* id) {
+    const int4* p = (const int4*)(ids + (s - base));
+    const int4 x = p[0], y = p[1];
+    id[0] = x.x; id[1] = x.y; id[2] = x.z; id[3] = x.w;
+    id[4] = y.x; id[5] = y.y; id[6] = y.z; id[7] = y.w;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(id[i]));
+  };
   // K operands of a chunk: key row hl of tile kt = slot s + 4kt + hl/4,
   // token hl%4, dims 32cc + 8gq.
   auto load_k = [&](int s, bf16x8 (*kf)[4]) {
+    const int q = hl >> 2;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const unsigned short* kr = ks + row_of(s + 4 * kt + (hl >> 2), hl & 3) * 128 + 8 * gq;
+      int bid = ids[s - base + 4 * kt + q];
+      asm volatile("" : "+v"(bid));
+      const uint32_t off = row_sel(s + 4 * kt + q, bid, hl & 3) * 256u + 16u * gq;
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
-        kf[kt][cc] = __builtin_bit_cast(bf16x8, *(const u16x8*)(kr + 32 * cc));
+      for (int cc = 0; cc < 4; ++cc) kf[kt][cc] = *(const bf16x8*)(kb + off + 64 * cc);
     }
   };
   // V of a chunk straight into LDS: instruction i moves slot s + i (1 KB);
-  // lane l's 16 bytes land at key 4i + l/16, chunk l%16 of that key row.
-  auto load_v = [&](int s, unsigned short* dst) {
+  // lane l's 16 bytes land at key 4i + l/16, chunk position l%16 of that key
+  // row, so the lane fetches the logical chunk stored there.
+  auto load_v = [&](int s, const int* id, unsigned short* dst) {
 #pragma unroll
     for (int i = 0; i < kSlotsPerChunk; ++i) {
       const int kk = 4 * i + (lane >> 4);
-      const int c = vswz(kk, lane & 15);  // logical chunk stored at this lane's position
-      const unsigned short* src = vsrc + row_of(s + i, lane >> 4) * 128 + 8 * c;
-      __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)(dst + i * 512), 16, 0,
-                                       0);
+      const uint32_t off = row_sel(s + i, id[i], lane >> 4) * 256u + 16u * vswz(kk, lane & 15);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(vb + off), (lds_void_t*)(dst + i * 512), 16,
+                                       0, 0);
     }
   };
 
@@ -176,24 +210,37 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
   f32x4 o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // m is the reference the exponentials are taken against: it follows the
+  // running maximum only when that grows by more than 2^8, so P <= 256 and
+  // the rescale of o and l is rare.
   float m = -INFINITY, l = 0.f;
 
-  bf16x8 kcur[2][4], knext[2][4];
-  if (s0 < s1) {
-    load_k(s0, kcur);
-    load_v(s0, vbuf);
-  }
-  int buf = 0;
-  for (int s = s0; s < s1; s += kSlotsPerChunk, buf ^= 1) {
-    const bool more = s + kSlotsPerChunk < s1;
-    if (more) {  // prefetch the next chunk while this one is computed
-      if (s + kSlotsPerChunk - base >= kIdWin) {
-        base = s + kSlotsPerChunk;
+  // Chunks are visited cyclically from a phase that grows with the query
+  // position (and so with the launch order): block lists are ascending, so
+  // the resident waves then read the same narrow window of the history at a
+  // time and share it in the caches.  The phase depends on the position, not
+  // on the launch index, so a chunked prefill sums in the same order.
+  // A wave loads one chunk (K to registers, V to LDS) and computes it; the
+  // latency is hidden by the other resident waves.
+  const int nch = (s1 - s0 + kSlotsPerChunk - 1) / kSlotsPerChunk;
+  int ph = 0;
+  if (!WIN && nsplit == 1 && resident > 0 && nch > 0)
+    ph = (int)(((R.pos * a.hkv + g) * nch / resident) % nch);
+  for (int cc = 0; cc < nch; ++cc) {
+    int c = ph + cc;
+    if (c >= nch) c -= nch;
+    const int s = s0 + kSlotsPerChunk * c;
+    if constexpr (WIN) {
+      if (s + kSlotsPerChunk - base > kIdWin) {
+        base = s;
         fill_ids(base);
       }
-      load_k(s + kSlotsPerChunk, knext);
-      load_v(s + kSlotsPerChunk, vbuf + (buf ^ 1) * 32 * 128);
     }
+    int id[8];
+    chunk_ids(s, id);
+    bf16x8 kc[2][4];
+    load_k(s, kc);
+    load_v(s, id, vbuf);
     // S^T tiles: lane holds head hl, keys 16kt + 4gq + i.
     f32x4 sacc[2];
 #pragma unroll
@@ -202,7 +249,7 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc)
         sacc[kt] =
-            __builtin_amdgcn_mfma_f32_16x16x32_bf16(kcur[kt][cc], qf[cc], sacc[kt], 0, 0, 0);
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc[kt][cc], qf[cc], sacc[kt], 0, 0, 0);
     }
     float sv[8];
 #pragma unroll
@@ -218,52 +265,72 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
 #pragma unroll
     for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
     mx = wave_max_xor(mx);
-    const float mn = fmaxf(m, mx);
-    const float alpha = exp2f(m - mn);
+    if (__ballot(mx > m + 8.f)) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = exp2f(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) o[tt] = o[tt] * alpha;
+      m = mn;
+    }
     float p[8], rs = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      p[j] = exp2f(sv[j] - mn);
+      p[j] = exp2f(sv[j] - m);
       rs += p[j];
     }
-    rs = wave_sum_xor(rs);
-    l = l * alpha + rs;
-    m = mn;
-    u16x8 pb;
+    l += wave_sum_xor(rs);
+    bf16x8 pf;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) pb[j] = f32_to_bf16(p[j]);
-    const bf16x8 pf = __builtin_bit_cast(bf16x8, pb);
-    // this chunk's V has landed once at most the next chunk's loads are pending
-    if (more)
-      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    const unsigned short* vs = vbuf + buf * 32 * 128;
+    for (int j = 0; j < 8; ++j) pf[j] = (__bf16)p[j];
     // O^T tile tt: A row = dim 16tt + hl, k index 8gq + j <-> key
-    // (j < 4 ? 4gq + j : 16 + 4gq + j - 4); B = P^T.
+    // (j < 4 ? 4gq + j : 16 + 4gq + j - 4), read transposed: lane hl of group
+    // gq addresses key 4gq + hl/4 (+16), dims 16tt + 4(hl%4) .. +3.
+    const unsigned short* vs = vbuf;
+    const int kk = 4 * gq + (hl >> 2);
+    const int e0 = 4 * (hl & 1);
+    uint32_t va[8];
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
-      u16x8 vv;
-      const int c = 2 * tt + (hl >> 3);
+      const int c = 2 * tt + ((hl & 3) >> 1);
+      va[tt] = lds_addr(vs + kk * 128 + vswz(kk, c) * 8 + e0);
+    }
+    s16x4 vr[16];
+    // wait until this chunk's V has landed, then read it all; the reads
+    // complete inside the block, before the next chunk's V is fetched
+    asm volatile(
+        "s_waitcnt vmcnt(0)\n"
+        "s_barrier\n"
+        "ds_read_b64_tr_b16 %0, %16\n"
+        "ds_read_b64_tr_b16 %1, %16 offset:4096\n"
+        "ds_read_b64_tr_b16 %2, %17\n"
+        "ds_read_b64_tr_b16 %3, %17 offset:4096\n"
+        "ds_read_b64_tr_b16 %4, %18\n"
+        "ds_read_b64_tr_b16 %5, %18 offset:4096\n"
+        "ds_read_b64_tr_b16 %6, %19\n"
+        "ds_read_b64_tr_b16 %7, %19 offset:4096\n"
+        "ds_read_b64_tr_b16 %8, %20\n"
+        "ds_read_b64_tr_b16 %9, %20 offset:4096\n"
+        "ds_read_b64_tr_b16 %10, %21\n"
+        "ds_read_b64_tr_b16 %11, %21 offset:4096\n"
+        "ds_read_b64_tr_b16 %12, %22\n"
+        "ds_read_b64_tr_b16 %13, %22 offset:4096\n"
+        "ds_read_b64_tr_b16 %14, %23\n"
+        "ds_read_b64_tr_b16 %15, %23 offset:4096\n"
+        "s_waitcnt lgkmcnt(0)\n"
+        : "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]),
+          "=&v"(vr[6]), "=&v"(vr[7]), "=&v"(vr[8]), "=&v"(vr[9]), "=&v"(vr[10]), "=&v"(vr[11]),
+          "=&v"(vr[12]), "=&v"(vr[13]), "=&v"(vr[14]), "=&v"(vr[15])
+        : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]),
+          "v"(va[7])
+        : "memory");
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int kk = (j < 4) ? (4 * gq + j) : (16 + 4 * gq + j - 4);
-        vv[j] = vs[kk * 128 + vswz(kk, c) * 8 + (hl & 7)];
-      }
-      o[tt] = o[tt] * alpha;
+    for (int tt = 0; tt < 8; ++tt) {
+      const s16x8 vv = __builtin_shufflevector(vr[2 * tt], vr[2 * tt + 1], 0, 1, 2, 3, 4, 5, 6, 7);
       o[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, o[tt],
                                                       0, 0, 0);
     }
-    __syncthreads();  // all reads of this buffer done before it is refilled
-    if (more) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) kcur[kt][cc] = knext[kt][cc];
-    }
   }
-
   if (nsplit == 1) {
     if (hl < G) {
       const float inv = 1.f / l;
@@ -271,13 +338,10 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
           (unsigned short*)a.out + (((int64_t)b * a.n_q + t) * a.hq + head) * 128;
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) {
-        unsigned short w4[4];
+        bf16x4 w;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w4[i] = f32_to_bf16(o[tt][i] * inv);
-        uint2 pk;
-        pk.x = (unsigned)w4[0] | ((unsigned)w4[1] << 16);
-        pk.y = (unsigned)w4[2] | ((unsigned)w4[3] << 16);
-        *(uint2*)(orow + 16 * tt + 4 * gq) = pk;
+        for (int i = 0; i < 4; ++i) w[i] = (__bf16)(o[tt][i] * inv);
+        *(bf16x4*)(orow + 16 * tt + 4 * gq) = w;
       }
     }
   } else {
@@ -477,17 +541,40 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, int nspli
   Elt<T>::st((T*)a.out, (((int64_t)b * a.n_q + t) * a.hq + h) * 128 + dim, tot / L);
 }
 
-// LDS of the bf16 kernel: two V chunks and a window of slot ids.
-static size_t bf16_lds_bytes() { return 2 * 32 * 128 * 2 + (size_t)kIdWin * 4; }
+// LDS of the bf16 kernel: one V chunk and a window of slot ids.
+static size_t bf16_lds_bytes() { return 32 * 128 * 2 + (size_t)kIdWin * 4; }
+
+// Waves of the prefill bf16 kernel resident on the whole device at once (the
+// period of its chunk phase), from the occupancy of the current device.
+static int resident_waves() {
+  static thread_local int dev_cached = -1, res_cached = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev == dev_cached) return res_cached;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_bf16_kernel<false>, 64,
+                                                   bf16_lds_bytes()) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  dev_cached = dev;
+  res_cached = per_cu * cus;
+  return res_cached;
+}
 
 static int decode_splits(int kB) { return (kB + 1 + kSlotsPerChunk - 1) / kSlotsPerChunk; }
 
 hipError_t launch_attn_prefill(qsa_dtype dt, const AttnArgs& a, hipStream_t st) {
   const int64_t waves = (int64_t)a.B * a.n_q * a.hkv;
   if (waves == 0) return hipSuccess;
-  if (dt == QSA_BF16)
-    hipLaunchKernelGGL(attn_bf16_kernel, dim3((unsigned)waves), dim3(64), bf16_lds_bytes(), st,
-                       a, 1, (float*)nullptr);
+  if (dt == QSA_BF16) {
+    // every slot id fits one window
+    if (a.kB + 1 + kSlotsPerChunk <= kIdWin)
+      hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3((unsigned)waves), dim3(64),
+                         bf16_lds_bytes(), st, a, 1, (float*)nullptr, resident_waves());
+    else
+      hipLaunchKernelGGL(attn_bf16_kernel<true>, dim3((unsigned)waves), dim3(64),
+                         bf16_lds_bytes(), st, a, 1, (float*)nullptr, 0);
+  }
   else
     hipLaunchKernelGGL(attn_f32_kernel, dim3((unsigned)waves), dim3(64), 0, st, a, 1,
                        (float*)nullptr);
@@ -504,8 +591,8 @@ hipError_t launch_attn_decode(qsa_dtype dt, const AttnArgs& a, void* ws, hipStre
   if (waves == 0) return hipSuccess;
   float* part = (float*)ws;
   if (dt == QSA_BF16)
-    hipLaunchKernelGGL(attn_bf16_kernel, dim3((unsigned)waves), dim3(64), bf16_lds_bytes(), st,
-                       a, nsplit, part);
+    hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3((unsigned)waves), dim3(64), bf16_lds_bytes(),
+                       st, a, nsplit, part, 0);
   else
     hipLaunchKernelGGL(attn_f32_kernel, dim3((unsigned)waves), dim3(64), 0, st, a, nsplit, part);
   hipError_t e = hipGetLastError();
