@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--prefill-cfg", default="cfg2")
     ap.add_argument("--decode-cfg", default="cfg4d")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1024,
+    ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="uniformly spaced prefill rows the CPU oracle computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -48,6 +48,29 @@ def parse():
                          "(3 times), so that a counter run can scale FETCH_SIZE / WRITE_SIZE "
                          "by a kernel of known traffic")
     return ap.parse_args()
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch of `kernel` recorded from rocprofv3 counter runs in
+    profiles/traffic.txt, if the kernel's source still has the recorded
+    sha256 (else None: the counters describe another version)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("#") or not line.strip():
+            continue
+        kv = dict(f.split("=", 1) for f in line.split())
+        if kv.get("kernel") != kernel:
+            continue
+        src = os.path.join(ROOT, kv["source"])
+        if not os.path.exists(src):
+            return None
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv["sha256"]:
+            return None
+        return int(kv["traffic_bytes"])
+    return None
 
 
 def sum_nb(n, r=4):
@@ -268,7 +291,9 @@ def main():
     else:
         ach = pre["attn_gbs"] if dom == 2 else pre["pool_gbs"]
         roof = dict(bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=ach / PEAK_HBM_GBS, traffic=None, kernel=names[dom])
+                    frac=ach / PEAK_HBM_GBS,
+                    traffic=recorded_traffic(names[dom]) if dom == 2 else None,
+                    kernel=names[dom])
     line = {
         "metric": METRIC,
         "value": pre["tok_s"],
