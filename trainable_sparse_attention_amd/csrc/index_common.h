@@ -211,6 +211,12 @@ template <> struct Mma32<unsigned short> {
     }
     return t;
   }
+  // B operands of step c of block row `row` (layout of load_b)
+  __device__ __forceinline__ static bf16x8 load_b_step(const unsigned short* stage, int row,
+                                                       int g, int c) {
+    const unsigned char* rb = (const unsigned char*)stage + row * 256;
+    return __builtin_bit_cast(bf16x8, *(const u32x4*)(rb + (((2 * c + g) ^ (row & 15)) << 4)));
+  }
   // lo operands of the NLO rotated steps of one row tile, in registers
   typedef u32x16 LoTile;
   template <int NLO>
@@ -247,6 +253,27 @@ template <> struct Mma32<unsigned short> {
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const bf16x8 bc = step(b, c);
+      if (c < NLO && c < 4) {
+        const u32x4 lv = {lo[4 * (c & 3)], lo[4 * (c & 3) + 1], lo[4 * (c & 3) + 2],
+                          lo[4 * (c & 3) + 3]};
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, lv), bc, acc, 0,
+                                                      0, 0);
+      }
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(step(a, c), bc, acc, 0, 0, 0);
+    }
+    return acc;
+  }
+  // one row tile against the B operands of block row `row` of an LDS stage,
+  // each step's operand read just before its MFMAs
+  template <int NLO>
+  __device__ __forceinline__ static f32x16 mma1_lds(const Tile& a, const LoTile& lo,
+                                                    const unsigned short* stage, int row, int g) {
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const bf16x8 bc = load_b_step(stage, row, g, c);
       if (c < NLO && c < 4) {
         const u32x4 lv = {lo[4 * (c & 3)], lo[4 * (c & 3) + 1], lo[4 * (c & 3) + 2],
                           lo[4 * (c & 3) + 3]};

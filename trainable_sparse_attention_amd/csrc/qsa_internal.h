@@ -77,6 +77,11 @@ struct IndexArgs {
 };
 
 size_t index_prefill_workspace(int B, int n_q, int num_cu, int kB);
+// the self-contained exact indexer over 128-row tiles [g0, g0 + count) (longest
+// first), optionally only those with only[tile - g0] != 0
+size_t index_exact_workspace(int B, int n_q, int num_cu);
+hipError_t launch_index_exact(qsa_dtype dt, const IndexArgs& a, void* ws, int num_cu, int g0,
+                              int count, const uint32_t* only, hipStream_t st);
 hipError_t launch_index_prefill(qsa_dtype dt, const IndexArgs& a, void* ws, int num_cu,
                                 hipStream_t st);
 size_t index_decode_workspace(int B, int n_q, int64_t nb_cap);
