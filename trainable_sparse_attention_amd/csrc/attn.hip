@@ -350,9 +350,10 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
       pp[hl] = m;
       pp[16 + hl] = l;
     }
+    if (hl < G) {  // padding heads are never read
 #pragma unroll
-    for (int tt = 0; tt < 8; ++tt)
-      *(f32x4*)(pp + 32 + hl * 128 + 16 * tt + 4 * gq) = o[tt];
+      for (int tt = 0; tt < 8; ++tt) *(f32x4*)(pp + 32 + hl * 128 + 16 * tt + 4 * gq) = o[tt];
+    }
   }
 }
 

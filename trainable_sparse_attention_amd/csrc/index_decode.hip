@@ -286,14 +286,8 @@ __global__ __launch_bounds__(kCollectThreads) void index_decode_collect(IndexArg
   const int b = row / a.n_q, t = row % a.n_q;
   const int64_t nb = dec_nb(a, b, t);
   if (nb <= a.kB || slice >= w.nslice) return;
-  const uint32_t* gh = w.ghist + (int64_t)row * kBins;
-  for (int e = tid; e < kBins; e += kCollectThreads) hist[e] = gh[e];
-  __syncthreads();
-  uint32_t above;
-  const int bin = block_find_bin<kCollectThreads>(hist, kBins, (uint32_t)a.kB, red, &above);
-  if (above + hist[bin] > (uint32_t)kCandCap) return;  // select takes the exact route
-  const uint32_t thr = (uint32_t)bin << 20;
-  // thread tid owns scores [s0 + 32 tid, s0 + 32 tid + 32) of this slice
+  // thread tid owns scores [s0 + 32 tid, s0 + 32 tid + 32) of this slice;
+  // they are fetched first, while the threshold is found
   const int64_t s0 = (int64_t)slice * kSliceLen;
   const int64_t e0 = s0 + (int64_t)kPerThread * tid;
   const float* src = w.scores + (int64_t)row * w.ld;
@@ -310,6 +304,13 @@ __global__ __launch_bounds__(kCollectThreads) void index_decode_collect(IndexArg
       for (int z = 0; z < 4; ++z) bits[j + z] = e + z < nb ? __float_as_uint(src[e + z]) : 0u;
     }
   }
+  const uint32_t* gh = w.ghist + (int64_t)row * kBins;
+  for (int e = tid; e < kBins; e += kCollectThreads) hist[e] = gh[e];
+  __syncthreads();
+  uint32_t above;
+  const int bin = block_find_bin<kCollectThreads>(hist, kBins, (uint32_t)a.kB, red, &above);
+  if (above + hist[bin] > (uint32_t)kCandCap) return;  // select takes the exact route
+  const uint32_t thr = (uint32_t)bin << 20;
   uint32_t mask = 0;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j)
@@ -475,15 +476,60 @@ __global__ __launch_bounds__(kSelThreads) void index_decode_select(IndexArgs a, 
     }
     c = (int)min(base, (uint32_t)kCandCap);
   }
-  // exact cut of the collected list by wave 0 (list is in ascending block order)
-  if (wv == 0) {
-    uint32_t v;
-    int krem;
-    wave_radix_kth([&](int e) { return (uint32_t)(cand[e] >> 32); }, c, (int)k, hist, lane, &v,
-                   &krem);
-    wave_keep_topk(cand, c, (int)k, v, krem, lane, 1, out, a.kB);
-    if (lane == 0) a.cnt[row] = (int)k;
+  // exact cut of the collected list (ascending block order) by the whole
+  // workgroup: radix select of the k-th score, then an ordered compaction
+  // (every score above it, and the first equal ones up to k)
+  __syncthreads();
+  uint32_t prefix = 0, pmask = 0;
+  uint32_t krem = k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int e = tid; e < 256; e += kSelThreads) hist[e] = 0;
+    __syncthreads();
+    for (int e = tid; e < c; e += kSelThreads) {
+      const uint32_t sb = (uint32_t)(cand[e] >> 32);
+      if ((sb & pmask) == prefix) atomicAdd(&hist[(sb >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    uint32_t ab;
+    const int digit = block_find_bin<kSelThreads>(hist, 256, krem, red, &ab);
+    krem -= ab;
+    prefix |= (uint32_t)digit << shift;
+    pmask |= 255u << shift;
+    __syncthreads();
   }
+  const uint32_t v = prefix;  // the k-th largest score; krem equal ones are kept
+  const uint64_t lt = lanemask_lt(lane);
+  uint32_t written = 0, eq_seen = 0;
+  for (int c0 = 0; c0 < c; c0 += kSelThreads) {
+    const int e = c0 + tid;
+    const uint64_t key = e < c ? cand[e] : 0ull;
+    const uint32_t sb = (uint32_t)(key >> 32);
+    const bool gt = e < c && sb > v;
+    const bool eq = e < c && sb == v;
+    const uint64_t beq = __ballot(eq);
+    if (lane == 0) red[NW + wv] = __popcll(beq);
+    __syncthreads();
+    uint32_t eq_before = eq_seen, eq_tot = 0;
+    for (int x = 0; x < NW; ++x) {
+      eq_before += x < wv ? red[NW + x] : 0u;
+      eq_tot += red[NW + x];
+    }
+    const bool keep = gt || (eq && eq_before + __popcll(beq & lt) < krem);
+    const uint64_t bk = __ballot(keep);
+    if (lane == 0) red[wv] = __popcll(bk);
+    __syncthreads();
+    uint32_t k_before = written, k_tot = 0;
+    for (int x = 0; x < NW; ++x) {
+      k_before += x < wv ? red[x] : 0u;
+      k_tot += red[x];
+    }
+    const uint32_t pos = k_before + __popcll(bk & lt);
+    if (keep && pos < k) out[pos] = (int32_t)(uint32_t)key;
+    written += k_tot;
+    eq_seen += eq_tot;
+    __syncthreads();
+  }
+  if (tid == 0) a.cnt[row] = (int)k;
 }
 
 hipError_t launch_index_decode(qsa_dtype dt, const IndexArgs& a, void* ws, hipStream_t st) {
