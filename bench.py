@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--prefill-cfg", default="cfg2")
     ap.add_argument("--decode-cfg", default="cfg4d")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=8192,
+    ap.add_argument("--cpu-rows", type=int, default=16384,
                     help="uniformly spaced prefill rows the CPU oracle computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
