@@ -46,7 +46,28 @@ def _index_gpu(p, q_idx, kbar, q_pos0=0, seq_len=None):
     ws = qsa.workspace(qsa.qsa_index_topk_workspace(p, qsa.dtype_code(q_idx), B, n_q,
                                                     kbar.shape[1], seq_len is not None))
     qsa.qsa_index_topk(p, q_idx, kbar, idx, cnt, ws, q_pos0, seq_len)
+    _assert_ids_valid(p, idx, cnt, q_pos0, seq_len)
     return idx, cnt
+
+
+def _assert_ids_valid(p, idx, cnt, q_pos0, seq_len):
+    """Every row's count is min(k_B, visible blocks) and its ids are distinct,
+    ascending and visible, padded with -1: checked on the host before any
+    kernel gathers through them."""
+    B, n_q, kB = idx.shape
+    g_idx, g_cnt = to_host(idx), to_host(cnt)
+    lens = to_host(seq_len) if seq_len is not None else None
+    for b in range(B):
+        off = int(lens[b]) - n_q if lens is not None else q_pos0
+        nvis = (off + np.arange(n_q) + 1) // p.r
+        k = np.minimum(kB, nvis)
+        assert np.array_equal(g_cnt[b], k), "index counts"
+        col = np.arange(kB)[None, :]
+        ids = g_idx[b]
+        live = col < k[:, None]
+        assert np.all(ids[~live] == -1), "index padding"
+        assert np.all((ids >= 0) & (ids < nvis[:, None]) | ~live), "index ids out of range"
+        assert np.all((np.diff(ids, axis=1) > 0) | ~live[:, 1:]), "index ids not ascending"
 
 
 def _attn_gpu(p, q, k, v, idx, cnt, q_pos0=0):
