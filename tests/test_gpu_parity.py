@@ -300,10 +300,12 @@ def _sample_rows(n, plants, seed=0, nrand=96):
                                      np.arange(n - 8, n), [pl[1] for pl in plants[:16]]]))
 
 
-@pytest.mark.parametrize("cfg", ["cfg1", "cfg2"])
+# cfg4p (1M tokens, 8192 query tiles) runs the indexer in four groups of
+# tiles that reuse one workspace; cfg1 and cfg2 fit one group
+@pytest.mark.parametrize("cfg", ["cfg1", "cfg2", "cfg4p"])
 def test_full_size_prefill_sampled(cfg):
     say("full-size prefill", cfg)
-    d = inputs.make(cfg, seed=100 + int(cfg[-1]), backend="torch")
+    d = inputs.make(cfg, seed={"cfg1": 101, "cfg2": 102, "cfg4p": 104}[cfg], backend="torch")
     p = _params()
     n = d["n"]
     kbar, idx, cnt, out = qsa.prefill(p, d["k_idx"], d["q_idx"], d["q"], d["k"], d["v"])
