@@ -259,6 +259,58 @@ def test_decode_parity(n_q, dtype):
         assert rel_err(g_out[b], o) <= TOL[dtype]
 
 
+def test_decode_step_graph_replays():
+    """A decode step (pool the newest block, index, attend) captured in a HIP
+    graph: every replay, with eager work and synchronizations between the
+    replays, equals the eager step bit for bit."""
+    say("decode step graph replays")
+    lens = [20000, 17001, 9003]
+    n = max(lens)
+    d = inputs.small(B=3, n=n, hq=16, hkv=2, dtype="bf16", seed=77)
+    p = _params()
+    t = _dev_inputs(d)
+    nbc = n // 4
+    kB = qsa.k_blocks(p)
+    kbar = _pool_gpu(p, t["k_idx"], nbc)
+    seq_len = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    qi = torch.stack([t["q_idx"][b, L - 1:L] for b, L in enumerate(lens)]).contiguous()
+    qq = torch.stack([t["q"][b, L - 1:L] for b, L in enumerate(lens)]).contiguous()
+    idx = torch.empty((3, 1, kB), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((3, 1), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(qq)
+    ws_i = qsa.workspace(qsa.qsa_index_topk_workspace(p, qsa.QSA_BF16, 3, 1, nbc, True))
+    ws_a = qsa.workspace(qsa.qsa_sparse_attn_decode_workspace(p, 3, 1, 16, 2))
+
+    def step():
+        qsa.qsa_pool_keys(p, t["k_idx"], kbar, nbc - 1, nbc)
+        qsa.qsa_index_topk(p, qi, kbar, idx, cnt, ws_i, 0, seq_len)
+        qsa.qsa_sparse_attn_decode(p, qq, t["k"], t["v"], seq_len, idx, cnt, out, ws_a)
+
+    step()
+    torch.cuda.synchronize()
+    _assert_ids_valid(p, idx, cnt, 0, seq_len)
+    ref = [x.clone() for x in (idx, cnt, out)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm the capture stream as torch asks
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        idx.fill_(-5)
+        cnt.fill_(-5)
+        out.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, x, r in zip(("idx", "cnt", "out"), (idx, cnt, out), ref):
+            assert torch.equal(x, r), "replay %d differs in %s" % (rep, name)
+
+
 def test_decode_exact_route_on_ties():
     """Decode rows whose scores tie in bulk: sequence 0 has a zero indexer
     query (every score is +0), sequence 1 a pooled cache whose keys are all
@@ -374,21 +426,25 @@ def test_full_size_decode_sampled(cfg, check):
 
 
 def test_threshold_fallback_rescan():
-    """White-box: rows that see more than 4032 blocks first estimate their
-    threshold from a strided sample of the blocks (the last tile of 128 rows
-    here samples m = 1024 blocks u * nbmin // m of the nbmin blocks its
-    first row sees).  Planting high scores exactly on those blocks for the
-    last row makes the estimate too high, so that row must be streamed again
-    exactly; the selection must still equal the oracle's."""
+    """White-box: a tile whose rows see more than 3072 blocks first scores a
+    strided sample of m = ceil(16 nbmin / k_B) blocks, u * nbmin // m, where
+    nbmin is what its first row sees; lane u % 32 keeps its two largest
+    sample scores per row, and the row's threshold is the
+    ceil(E + 5 sqrt(E) + 2)-th largest kept value (E = m k_B / visible,
+    about 16, so the 38th).  Planting high scores on the first 100 sampled
+    blocks for the last row fills every lane's two slots with planted scores,
+    so the threshold lands among the planted scores and fewer than k_B blocks
+    pass it: the tile is flagged and recomputed by the exact kernel, and the
+    selection must still equal the oracle's."""
     say("threshold fallback")
     n = 20480
     d = inputs.small(B=1, n=n, hq=4, hkv=1, dtype="bf16", seed=77)
     i = n - 1
     row0 = (n - 1) // 128 * 128
     nbmin = (row0 + 1) // 4
-    m = max(1024, min(2048, nbmin // 16))
+    m = min(max(-(-16 * nbmin // 512), 64), nbmin)
     sample = [u * nbmin // m for u in range(m)]
-    planted = sample[::5][:200]  # distinct high scores on 200 sampled blocks
+    planted = sample[:100]  # distinct high scores; every lane sees three or more
     qf = inputs.bf16_bits_to_f32(d["q_idx"][0, i, 0])
     kf = inputs.bf16_bits_to_f32(d["k_idx"][0])
     for u, blk in enumerate(planted):
@@ -398,13 +454,22 @@ def test_threshold_fallback_rescan():
     p = _params()
     t = _dev_inputs(d)
     kbar = _pool_gpu(p, t["k_idx"], n // 4)
-    idx, cnt = _index_gpu(p, t["q_idx"], kbar)
+    kB = qsa.k_blocks(p)
+    idx = torch.empty((1, n, kB), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((1, n), dtype=torch.int32, device="cuda")
+    ws = qsa.workspace(qsa.qsa_index_topk_workspace(p, qsa.QSA_BF16, 1, n, n // 4, False))
+    qsa.qsa_index_topk(p, t["q_idx"], kbar, idx, cnt, ws)
     torch.cuda.synchronize()
+    _assert_ids_valid(p, idx, cnt, 0, None)
+    # the workspace ends with one flag per tile of the group (256-byte
+    # aligned); the tiles run longest first, so the last tile is flag 0
+    ntiles = n // 128
+    flags_off = ws.numel() - (ntiles * 4 + 255) // 256 * 256
+    flags = to_host(ws[flags_off:flags_off + ntiles * 4]).view(np.uint32)
+    assert flags[0] != 0, "the planted tile was not flagged for the exact kernel"
     kbar_h, g_idx, g_cnt = to_host(kbar), to_host(idx), to_host(cnt)
     rows = np.arange(row0, n)
     near, o_idx, _ = _check_index_rows(0, rows, g_idx, g_cnt, d["q_idx"][0], kbar_h[0], 2048)
-    # the threshold estimate (the j-th largest sample score, j < 200) left
-    # fewer than k_B candidates: the rescan must recover all planted blocks
-    # plus the best noise blocks
+    # the exact kernel recovers all planted blocks plus the best noise blocks
     assert set(planted) <= set(g_idx[0, i, :g_cnt[0, i]].tolist())
     assert g_cnt[0, i] == 512
