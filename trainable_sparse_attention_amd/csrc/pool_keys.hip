@@ -4,11 +4,23 @@
 //
 // HBM-bound stream: each block reads r * d_idx inputs and writes d_idx
 // outputs.  One 64-lane wave per block; lane c covers dims c and c + 64.
+// A decode step pools one block per sequence, where the fp64 angle
+// reduction, not the bytes, sets the time: it overlaps the key loads.
 // Means are taken in float, the rotation in float with cos/sin formed from
 // a double angle, and the result is rounded once to the storage type.
 #include "qsa_internal.h"
 
 namespace qsa {
+
+__device__ __forceinline__ uint32_t raw_bits(unsigned short x) { return x; }
+__device__ __forceinline__ uint32_t raw_bits(float x) { return __float_as_uint(x); }
+template <typename T> __device__ __forceinline__ float from_bits(uint32_t x);
+template <> __device__ __forceinline__ float from_bits<unsigned short>(uint32_t x) {
+  return __uint_as_float(x << 16);
+}
+template <> __device__ __forceinline__ float from_bits<float>(uint32_t x) {
+  return __uint_as_float(x);
+}
 
 template <typename T>
 __global__ __launch_bounds__(256) void pool_keys_kernel(const T* __restrict__ k_idx,
@@ -21,30 +33,56 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(const T* __restrict__ k_
   const int wv = threadIdx.x >> 6;
   const int64_t job = (int64_t)blockIdx.x * 4 + wv;  // (sequence, block) pair
   const bool live = job < (int64_t)B * nblk;
-  int64_t b = 0, j = 0;
+  const int64_t b = live ? job / nblk : 0, j = live ? b0 + job % nblk : 0;
+  const int64_t pos = (j + 1) * r - 1;
+  const int half = R / 2;
+  // the first four keys of the block are loaded, then the rotation factors
+  // of this lane's columns c = lane, lane + 64 (those below R) are formed
+  // while the loads are in flight
+  const T* src = k_idx + ((int64_t)b * n_cap + j * r) * 128;
+  // (token min(t, r - 1): every load stays inside the block and none waits
+  // on a per-load branch; the sum below takes only tokens t < r)
+  uint32_t v[2][4] = {};  // raw bits: converted only after the factors exist
   if (live) {
-    b = job / nblk;
-    j = b0 + job % nblk;
-    const T* src = k_idx + ((int64_t)b * n_cap + j * r) * 128;
-    for (int c = lane; c < 128; c += 64) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        v[i][t] = raw_bits(src[(int64_t)min(t, r - 1) * 128 + lane + 64 * i]);
+  }
+  float cs[2] = {1.f, 1.f}, sn[2] = {0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = lane + 64 * i;
+    if (live && c < R) rope_cs(pos, c < half ? c : c - half, R, log2_theta, &cs[i], &sn[i]);
+  }
+  // the raw values pass through an empty asm that also reads the factors,
+  // so the wait for the loads is placed after the factors are formed
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      asm volatile("" : "+v"(v[i][t]) : "v"(cs[0]), "v"(sn[0]), "v"(cs[1]), "v"(sn[1]));
+  if (live) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
       float s = 0.f;
-      for (int t = 0; t < r; ++t) s += Elt<T>::ld(src, (int64_t)t * 128 + c);
-      mean_s[wv][c] = s / (float)r;
+      for (int t = 0; t < r; ++t)
+        s += t < 4 ? from_bits<T>(v[i][t]) : Elt<T>::ld(src, (int64_t)t * 128 + lane + 64 * i);
+      mean_s[wv][lane + 64 * i] = s / (float)r;
     }
   }
   __syncthreads();
   if (!live) return;
-  const int64_t pos = (j + 1) * r - 1;
-  const int half = R / 2;
   T* dst = kbar + ((int64_t)b * nb_cap + j) * 128;
-  for (int c = lane; c < 128; c += 64) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = lane + 64 * i;
     float out;
     if (c < R) {
       const int jj = c < half ? c : c - half;
-      float cs, sn;
-      rope_cs(pos, jj, R, log2_theta, &cs, &sn);
       const float a = mean_s[wv][jj], bb = mean_s[wv][jj + half];
-      out = c < half ? (a * cs - bb * sn) : (a * sn + bb * cs);
+      out = c < half ? (a * cs[i] - bb * sn[i]) : (a * sn[i] + bb * cs[i]);
     } else {
       out = mean_s[wv][c];
     }
