@@ -542,8 +542,36 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, int nspli
   Elt<T>::st((T*)a.out, (((int64_t)b * a.n_q + t) * a.hq + h) * 128 + dim, tot / L);
 }
 
-// LDS of the bf16 kernel: one V chunk and a window of slot ids.
-static size_t bf16_lds_bytes() { return 32 * 128 * 2 + (size_t)kIdWin * 4; }
+// LDS the bf16 kernel uses: one V chunk and a window of slot ids.
+static size_t bf16_lds_need() { return 32 * 128 * 2 + (size_t)kIdWin * 4; }
+
+// Waves of the prefill bf16 kernel allowed on one CU.  Fewer concurrent waves
+// keep the window of the history that the resident waves read at one time
+// small enough to be shared in L2; enough remain to keep the gathers in
+// flight (256K-token prefill: 15 waves per CU 45.1 ms, 10 41.1, 8 39.5,
+// 7 39.1, 6 46.8).  The LDS each wave requests enforces the limit.
+constexpr int kPrefillWavesPerCu = 7;
+
+// LDS requested per prefill wave: what the kernel uses, or the CU's LDS
+// shared by kPrefillWavesPerCu waves if that is more.
+static size_t bf16_lds_prefill() {
+  static thread_local int dev_cached = -1;
+  static thread_local size_t cached = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return bf16_lds_need();
+  if (dev == dev_cached) return cached;
+  int per_cu = 0;
+  size_t bytes = bf16_lds_need();
+  if (hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) ==
+          hipSuccess &&
+      per_cu > 0) {
+    const size_t share = ((size_t)per_cu / kPrefillWavesPerCu) & ~(size_t)255;
+    if (share > bytes) bytes = share;
+  }
+  dev_cached = dev;
+  cached = bytes;
+  return cached;
+}
 
 // Waves of the prefill bf16 kernel resident on the whole device at once (the
 // period of its chunk phase), from the occupancy of the current device.
@@ -554,7 +582,7 @@ static int resident_waves() {
   if (dev == dev_cached) return res_cached;
   int per_cu = 0, cus = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_bf16_kernel<false>, 64,
-                                                   bf16_lds_bytes()) != hipSuccess ||
+                                                   bf16_lds_prefill()) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
   dev_cached = dev;
@@ -571,10 +599,10 @@ hipError_t launch_attn_prefill(qsa_dtype dt, const AttnArgs& a, hipStream_t st) 
     // every slot id fits one window
     if (a.kB + 1 + kSlotsPerChunk <= kIdWin)
       hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3((unsigned)waves), dim3(64),
-                         bf16_lds_bytes(), st, a, 1, (float*)nullptr, resident_waves());
+                         bf16_lds_prefill(), st, a, 1, (float*)nullptr, resident_waves());
     else
       hipLaunchKernelGGL(attn_bf16_kernel<true>, dim3((unsigned)waves), dim3(64),
-                         bf16_lds_bytes(), st, a, 1, (float*)nullptr, 0);
+                         bf16_lds_prefill(), st, a, 1, (float*)nullptr, 0);
   }
   else
     hipLaunchKernelGGL(attn_f32_kernel, dim3((unsigned)waves), dim3(64), 0, st, a, 1,
@@ -592,7 +620,7 @@ hipError_t launch_attn_decode(qsa_dtype dt, const AttnArgs& a, void* ws, hipStre
   if (waves == 0) return hipSuccess;
   float* part = (float*)ws;
   if (dt == QSA_BF16)
-    hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3((unsigned)waves), dim3(64), bf16_lds_bytes(),
+    hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3((unsigned)waves), dim3(64), bf16_lds_need(),
                        st, a, nsplit, part, 0);
   else
     hipLaunchKernelGGL(attn_f32_kernel, dim3((unsigned)waves), dim3(64), 0, st, a, nsplit, part);
