@@ -548,9 +548,10 @@ static size_t bf16_lds_need() { return 32 * 128 * 2 + (size_t)kIdWin * 4; }
 // Waves of the prefill bf16 kernel allowed on one CU.  Fewer concurrent waves
 // keep the window of the history that the resident waves read at one time
 // small enough to be shared in L2; enough remain to keep the gathers in
-// flight (256K-token prefill: 15 waves per CU 45.1 ms, 10 41.1, 8 39.5,
-// 7 39.1, 6 46.8).  The LDS each wave requests enforces the limit.
-constexpr int kPrefillWavesPerCu = 7;
+// flight, two per SIMD (256K-token prefill step, attention: 15 waves per CU
+// 45.4 ms, 10 41.0, 9 40.7, 8 39.5, 7 41.7, 6 46.8).  The LDS each wave
+// requests enforces the limit.
+constexpr int kPrefillWavesPerCu = 8;
 
 // LDS requested per prefill wave: what the kernel uses, or the CU's LDS
 // shared by kPrefillWavesPerCu waves if that is more.
