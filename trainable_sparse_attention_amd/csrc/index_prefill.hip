@@ -344,11 +344,48 @@ __global__ __launch_bounds__(kCutWaves * 64) void index_cut_kernel(IndexArgs a, 
   } else if (c == k) {  // everything is kept: copy in order
     for (int e = lane; e < a.kB; e += 64) out[e] = e < c ? (int32_t)(uint32_t)list[e] : -1;
   } else {
-    stage_scores(list, c, lsc[wv], lane);
+    // One read of the list: lane holds entries lane + 64 j; their scores go
+    // to LDS for the radix select, their block ids stay in registers for the
+    // order-preserving keep pass.
+    constexpr int J = kList / 64;
+    uint32_t klo[J], khi[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int e = lane + 64 * j;
+      const uint64_t key = e < c ? list[e] : 0ull;
+      klo[j] = (uint32_t)key;
+      khi[j] = (uint32_t)(key >> 32);
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int e = lane + 64 * j;
+      if (e < c) lsc[wv][e] = khi[j];
+    }
+    wave_sync();
     uint32_t v;
     int krem;
     wave_radix_kth([&](int e) { return lsc[wv][e]; }, c, k, hist[wv], lane, &v, &krem);
-    wave_keep_topk(list, c, k, v, krem, lane, 1, out, a.kB);
+    // the top k in block order: every score above v, then the first krem
+    // scores equal to v (smaller block ids win ties)
+    const uint64_t lt = lanemask_lt(lane);
+    int written = 0, eq_seen = 0;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      if (64 * j >= c) break;
+      const int e = lane + 64 * j;
+      const bool valid = e < c;
+      const bool gt = valid && khi[j] > v;
+      const bool eq = valid && khi[j] == v;
+      const uint64_t beq = __ballot(eq);
+      const int eq_rank = eq_seen + __popcll(beq & lt);
+      const bool keep = gt || (eq && eq_rank < krem);
+      const uint64_t bk = __ballot(keep);
+      const int pos = written + __popcll(bk & lt);
+      if (keep && pos < k) out[pos] = (int32_t)klo[j];
+      written += __popcll(bk);
+      eq_seen += __popcll(beq);
+    }
+    for (int e = k + lane; e < a.kB; e += 64) out[e] = -1;
   }
   if (lane == 0) a.cnt[(int64_t)G.b * a.n_q + t] = k;
 }
