@@ -37,12 +37,11 @@ constexpr int kScanWaves = 16;             // 8 rows (one 32-row MFMA tile) per 
 constexpr int kStageBytes = 32768;         // one LDS stage: 128 pooled keys (bf16)
 constexpr int kStageBlk = 128;
 constexpr int kList = 3072;                // candidate list capacity per row
-constexpr int kBuf = 448;                  // LDS append buffer per wave (entries)
+constexpr int kBuf = 384;                  // LDS append buffer per wave (16-byte entries)
 constexpr int kGroupTiles = 2048;
 constexpr float kSampleE = 16.f;           // expected top-k_B blocks in a sample
 constexpr int kCutWaves = 4;
-constexpr uint32_t kNoSlot = 0xffffffffu;  // buffered append past a full list
-constexpr int kScanLds = 2 * kStageBytes + kScanWaves * kBuf * 12;
+constexpr int kScanLds = 2 * kStageBytes + kScanWaves * kBuf * 16;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
@@ -105,8 +104,8 @@ __global__ __launch_bounds__(1024, 1) void index_scan_kernel(IndexArgs a, PipeWs
   };
   unsigned short* stage0 = (unsigned short*)smem;
   unsigned short* stage1 = (unsigned short*)(smem + kStageBytes);
-  uint32_t* boff = (uint32_t*)(smem + 2 * kStageBytes) + wv * kBuf;
-  uint64_t* bkey = (uint64_t*)(smem + 2 * kStageBytes + kScanWaves * kBuf * 4) + wv * kBuf;
+  // staged appends: (list entry, block id, score bits, unused)
+  u32x4* bent = (u32x4*)(smem + 2 * kStageBytes) + wv * kBuf;
 
   // ---- prologue: rotated queries -> the wave's A tile (hi and lo) --------
   const int half = a.R / 2;
@@ -184,16 +183,14 @@ __global__ __launch_bounds__(1024, 1) void index_scan_kernel(IndexArgs a, PipeWs
   }
   // every row of the wave sees blocks below nb_all (0 if some row is absent)
   const int nb_all = wave_rows == 8 ? nb0 / a.r : 0;
-  const uint32_t lt32 = (1u << col) - 1u;
-  const uint64_t lt64 = lanemask_lt(lane);
   const unsigned short* kb = (const unsigned short*)a.kbar + (size_t)G.b * a.nb_cap * 128;
 
   int nbuf = 0;
   auto flush = [&]() {
     wave_sync();
     for (int e = lane; e < nbuf; e += 64) {
-      const uint32_t o = boff[e];
-      if (o != kNoSlot) w.list[o] = bkey[e];
+      const u32x4 x = bent[e];
+      w.list[x.x] = ((uint64_t)x.z << 32) | x.y;
     }
     nbuf = 0;
     wave_sync();
@@ -260,21 +257,27 @@ __global__ __launch_bounds__(1024, 1) void index_scan_kernel(IndexArgs a, PipeWs
         }
         const bool any = pass[0] || pass[1] || pass[2] || pass[3];
         if (__ballot(any)) {
+          // a passing lane's rank in the wave (mbcnt) gives its buffer
+          // position; minus the passing lanes of the other row group below
+          // it, its place in its row's list.  Past a full list the entry goes
+          // to the list's last place: the row's count then exceeds kList and
+          // the row fails, whatever the list holds.
           int pos = nbuf;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const uint64_t bal = __ballot(pass[j]);
-            if (bal) {
-              if (pass[j]) {
-                const uint32_t grp = (uint32_t)(bal >> (32 * g));
-                const int slot = cnt[j] + __popc(grp & lt32);
-                const int p = pos + __popcll(bal & lt64);
-                boff[p] = slot < kList ? lbase0 + (uint32_t)(2 * j * kList + slot) : kNoSlot;
-                bkey[p] = ((uint64_t)__float_as_uint(sc[j]) << 32) | (uint32_t)blk;
-              }
-              cnt[j] += __popc((uint32_t)(bal >> (32 * g)));
-              pos += __popcll(bal);
+            const uint32_t n_lo = (uint32_t)__popc((uint32_t)bal);
+            const uint32_t n_hi = (uint32_t)__popc((uint32_t)(bal >> 32));
+            const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
+                (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+            if (pass[j]) {
+              const uint32_t slot = (uint32_t)cnt[j] + rank - (g ? n_lo : 0u);
+              bent[pos + rank] =
+                  u32x4{lbase0 + (uint32_t)(2 * j * kList) + min(slot, (uint32_t)kList - 1u),
+                        (uint32_t)blk, __float_as_uint(sc[j]), 0u};
             }
+            cnt[j] += (int)(g ? n_hi : n_lo);
+            pos += (int)(n_lo + n_hi);
           }
           nbuf = pos;
         }
