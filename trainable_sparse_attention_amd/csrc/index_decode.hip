@@ -115,6 +115,16 @@ __global__ __launch_bounds__(256) void index_decode_prep(IndexArgs a, DecodeWs w
   const int row = blockIdx.x, b = row / a.n_q, t = row % a.n_q;
   const int half = a.R / 2;
   const int64_t pos = dec_pos(a, b, t);
+  // the query values are loaded first; the angles are formed while they fly
+  const T* qr0 = (const T*)a.q_idx + (int64_t)row * 4 * 128;
+  float xv[2], yv[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {  // elements tid and tid + 256 of the 4 x 128
+    const int e = tid + 256 * k, hh = e >> 7, d = e & 127;
+    const T* qr = qr0 + hh * 128;
+    xv[k] = Elt<T>::ld(qr, d);
+    yv[k] = d < a.R ? Elt<T>::ld(qr, d < half ? d + half : d - half) : 0.f;
+  }
   for (int j = tid; j < half; j += 256) {
     float c, s;
     rope_cs(pos < 0 ? 0 : pos, j, a.R, a.log2_theta, &c, &s);
@@ -124,17 +134,14 @@ __global__ __launch_bounds__(256) void index_decode_prep(IndexArgs a, DecodeWs w
   for (int e = tid; e < kBins; e += 256) h[e] = 0;
   if (tid == 0) w.gfill[row] = 0;
   __syncthreads();
-  const T* qr0 = (const T*)a.q_idx + (int64_t)row * 4 * 128;
   float* dst = w.qrot + (int64_t)row * 4 * 128;
-  for (int e = tid; e < 4 * 128; e += 256) {
-    const int hh = e >> 7, d = e & 127;
-    const T* qr = qr0 + hh * 128;
-    const float x = Elt<T>::ld(qr, d);
-    float val = x;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int e = tid + 256 * k, d = e & 127;
+    float val = xv[k];
     if (d < a.R) {
       const float2 cs = table[d < half ? d : d - half];
-      const float y = Elt<T>::ld(qr, d < half ? d + half : d - half);
-      val = d < half ? (x * cs.x - y * cs.y) : (y * cs.y + x * cs.x);
+      val = d < half ? (xv[k] * cs.x - yv[k] * cs.y) : (yv[k] * cs.y + xv[k] * cs.x);
     }
     dst[e] = val;
   }
