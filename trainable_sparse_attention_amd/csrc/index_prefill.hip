@@ -128,27 +128,38 @@ __global__ __launch_bounds__(1024, 1) void index_scan_kernel(IndexArgs a, PipeWs
   {
     const float2* table = (const float2*)(smem + 2 * kStageBytes);
     float* scr = (float*)smem + wv * 8 * 128;  // 8 A rows in float
-    const unsigned short* qsrc = (const unsigned short*)a.q_idx;
+    // the wave's queries (8 x 4 heads x 128 bf16) are one contiguous 8 KB
+    // run; four queries at a time go to LDS (load j of a lane brings 16
+    // bytes of query j, all four in flight together; absent queries read as
+    // zeros) for the rotation, which pairs dims across lanes
+    const uint4* qw = (const uint4*)a.q_idx + ((int64_t)G.b * a.n_q + G.row0 + 8 * wv) * 64;
+    uint4* rawq = (uint4*)(smem + 2 * kStageBytes + 32768) + wv * 256;
 #pragma unroll 1
     for (int hf = 0; hf < 4; ++hf) {
+      if ((hf & 1) == 0) {
+        uint4 rq[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int ql = 2 * hf + j;
+          rq[j] = G.row0 + 8 * wv + ql < a.n_q ? qw[ql * 64 + lane] : uint4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rawq[j * 64 + lane] = rq[j];
+        wave_sync();
+      }
+      const unsigned short* raw16 = (const unsigned short*)(rawq + (hf & 1) * 128);
       // A rows 8 hf .. 8 hf + 7 = queries 2 hf, 2 hf + 1 (rows 4q + h)
       for (int e = lane; e < 8 * 128; e += 64) {
         const int rr = e >> 7, d = e & 127;
-        const int m = 8 * hf + rr;
-        const int ql = 8 * wv + (m >> 2), hh = m & 3;
-        const int t = G.row0 + ql;
-        float val = 0.f;
-        if (t < a.n_q) {
-          const unsigned short* qr = qsrc + (((int64_t)G.b * a.n_q + t) * 4 + hh) * 128;
-          const float x = bf16_to_f32(qr[d]);
-          if (d < a.R) {
-            const int j = d < half ? d : d - half;
-            const float2 cs = table[ql * half + j];
-            const float y = bf16_to_f32(qr[d < half ? d + half : d - half]);
-            val = d < half ? (x * cs.x - y * cs.y) : (y * cs.y + x * cs.x);
-          } else {
-            val = x;
-          }
+        const int ql = 8 * wv + ((8 * hf + rr) >> 2);
+        const unsigned short* qr = raw16 + rr * 128;  // query 2 hf + rr / 4, head rr % 4
+        const float x = bf16_to_f32(qr[d]);
+        float val = x;
+        if (d < a.R) {
+          const int j = d < half ? d : d - half;
+          const float2 cs = table[ql * half + j];
+          const float y = bf16_to_f32(qr[d < half ? d + half : d - half]);
+          val = d < half ? (x * cs.x - y * cs.y) : (y * cs.y + x * cs.x);
         }
         scr[e] = val;
       }
@@ -199,6 +210,10 @@ __global__ __launch_bounds__(1024, 1) void index_scan_kernel(IndexArgs a, PipeWs
   // 1 KB at (2 wv + i) KB; lane l's 16 bytes land at l * 16 within it, so the
   // lane loads the chunk that belongs there after the swizzle (chunk c of
   // block row r is stored at chunk c ^ (r & 15)).
+  // the wave index as a scalar: the stage's LDS destination then stays in
+  // scalar registers rather than in a spilled vector register, whose reload
+  // would wait for the append stores just issued
+  const int wv_s = __builtin_amdgcn_readfirstlane(wv);
   auto issue = [&](int s, unsigned short* st) {
     int ln = __lane_id();
     asm volatile("" : "+v"(ln));
@@ -211,7 +226,7 @@ __global__ __launch_bounds__(1024, 1) void index_scan_kernel(IndexArgs a, PipeWs
       const int blk = u < len ? block_of(u) : 0;
       const unsigned short* src = kb + (size_t)blk * 128 + lch * 8;
       __builtin_amdgcn_global_load_lds((glb_void_t*)src,
-                                       (lds_void_t*)(st + (wv * 2 + i) * 512), 16, 0, 0);
+                                       (lds_void_t*)(st + (wv_s * 2 + i) * 512), 16, 0, 0);
     }
   };
 
