@@ -87,7 +87,10 @@ __global__ __launch_bounds__(1024, 1) void index_scan_kernel(IndexArgs a, PipeWs
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   typedef Mma32<unsigned short> M;
   const int tid = threadIdx.x;
-  const int wv = tid >> 6, lane = tid & 63, col = lane & 31, g = lane >> 5;
+  // the wave index as a scalar, so that what derives from it (row counts,
+  // the causal edge, the stage's LDS destination) stays wave-uniform
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, col = lane & 31, g = lane >> 5;
   const int Lg = blockIdx.x;
   const TileGeo G = tile_geo(a, g0 + Lg, ntiles);
   if (SAMPLE) {
@@ -181,7 +184,8 @@ __global__ __launch_bounds__(1024, 1) void index_scan_kernel(IndexArgs a, PipeWs
   const int rbase = G.row0 + 8 * wv;
   const int wave_rows = min(8, a.n_q - rbase);
   float tau[4], t1[4], t2[4];  // t1 >= t2: the lane's two largest sample scores
-  int cnt[4];
+  // entries appended to rows 2j (cnt_lo) and 2j + 1 (cnt_hi): wave-uniform
+  int cnt_lo[4], cnt_hi[4];
   // list of row q = 2j + g starts at lbase0 + 2j kList; row q sees (nb0 + q) / r
   const uint32_t lbase0 = (uint32_t)(Lg * kTileRows + 8 * wv + g) * (uint32_t)kList;
   const int nb0 = (int)(G.seq_off + rbase + 1);
@@ -190,7 +194,7 @@ __global__ __launch_bounds__(1024, 1) void index_scan_kernel(IndexArgs a, PipeWs
     const int q = 2 * j + g;
     tau[j] = SAMPLE ? 0.f : (q < wave_rows ? w.tau[Lg * kTileRows + 8 * wv + q] : 0.f);
     t1[j] = t2[j] = 0.f;
-    cnt[j] = 0;
+    cnt_lo[j] = cnt_hi[j] = 0;
   }
   // every row of the wave sees blocks below nb_all (0 if some row is absent)
   const int nb_all = wave_rows == 8 ? nb0 / a.r : 0;
@@ -210,10 +214,6 @@ __global__ __launch_bounds__(1024, 1) void index_scan_kernel(IndexArgs a, PipeWs
   // 1 KB at (2 wv + i) KB; lane l's 16 bytes land at l * 16 within it, so the
   // lane loads the chunk that belongs there after the swizzle (chunk c of
   // block row r is stored at chunk c ^ (r & 15)).
-  // the wave index as a scalar: the stage's LDS destination then stays in
-  // scalar registers rather than in a spilled vector register, whose reload
-  // would wait for the append stores just issued
-  const int wv_s = __builtin_amdgcn_readfirstlane(wv);
   auto issue = [&](int s, unsigned short* st) {
     int ln = __lane_id();
     asm volatile("" : "+v"(ln));
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(1024, 1) void index_scan_kernel(IndexArgs a, PipeWs
       const int blk = u < len ? block_of(u) : 0;
       const unsigned short* src = kb + (size_t)blk * 128 + lch * 8;
       __builtin_amdgcn_global_load_lds((glb_void_t*)src,
-                                       (lds_void_t*)(st + (wv_s * 2 + i) * 512), 16, 0, 0);
+                                       (lds_void_t*)(st + (wv * 2 + i) * 512), 16, 0, 0);
     }
   };
 
@@ -249,17 +249,10 @@ __global__ __launch_bounds__(1024, 1) void index_scan_kernel(IndexArgs a, PipeWs
         const int u = u0 + col;
         const int blk = u < len ? block_of(u) : 0x7fffffff;
         float sc[4];
-        bool pass[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 4; ++j)
           sc[j] = relu(acc[4 * j]) + relu(acc[4 * j + 1]) + relu(acc[4 * j + 2]) +
                   relu(acc[4 * j + 3]);
-          pass[j] = sc[j] >= tau[j];
-        }
-        if (u0 + 32 > nb_all || u0 + 32 > len) {  // causal edge of the wave (uniform)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) pass[j] = pass[j] && (blk < (nb0 + 2 * j + g) / a.r);
-        }
         if constexpr (SAMPLE) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -270,29 +263,38 @@ __global__ __launch_bounds__(1024, 1) void index_scan_kernel(IndexArgs a, PipeWs
           }
           continue;
         }
-        const bool any = pass[0] || pass[1] || pass[2] || pass[3];
-        if (__ballot(any)) {
+        // bal[j]: the lanes whose score for row 2j + g passes (low half: row
+        // 2j, high half: row 2j + 1)
+        uint64_t bal[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bal[j] = __ballot(sc[j] >= tau[j]);
+        if (u0 + 32 > nb_all || u0 + 32 > len) {  // causal edge of the wave (uniform)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bal[j] &= __ballot(blk < (nb0 + 2 * j + g) / a.r);
+        }
+        if (bal[0] | bal[1] | bal[2] | bal[3]) {
           // a passing lane's rank in the wave (mbcnt) gives its buffer
-          // position; minus the passing lanes of the other row group below
-          // it, its place in its row's list.  Past a full list the entry goes
-          // to the list's last place: the row's count then exceeds kList and
-          // the row fails, whatever the list holds.
+          // position; minus the passing lanes of the low half when it is in
+          // the high half, its place in its row's list.  Past a full list the
+          // entry goes to the list's last place: the row's count then exceeds
+          // kList and the row fails, whatever the list holds.
           int pos = nbuf;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const uint64_t bal = __ballot(pass[j]);
-            const uint32_t n_lo = (uint32_t)__popc((uint32_t)bal);
-            const uint32_t n_hi = (uint32_t)__popc((uint32_t)(bal >> 32));
-            const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
-                (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-            if (pass[j]) {
-              const uint32_t slot = (uint32_t)cnt[j] + rank - (g ? n_lo : 0u);
+            if (bal[j] == 0) continue;
+            const uint32_t lo = (uint32_t)bal[j], hi = (uint32_t)(bal[j] >> 32);
+            const int n_lo = __popc(lo), n_hi = __popc(hi);
+            if (__builtin_amdgcn_inverse_ballot_w64(bal[j])) {
+              const uint32_t rank =
+                  __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
+              const uint32_t slot = (uint32_t)(g ? cnt_hi[j] - n_lo : cnt_lo[j]) + rank;
               bent[pos + rank] =
                   u32x4{lbase0 + (uint32_t)(2 * j * kList) + min(slot, (uint32_t)kList - 1u),
                         (uint32_t)blk, __float_as_uint(sc[j]), 0u};
             }
-            cnt[j] += (int)(g ? n_hi : n_lo);
-            pos += (int)(n_lo + n_hi);
+            cnt_lo[j] += n_lo;
+            cnt_hi[j] += n_hi;
+            pos += n_lo + n_hi;
           }
           nbuf = pos;
         }
@@ -332,7 +334,8 @@ __global__ __launch_bounds__(1024, 1) void index_scan_kernel(IndexArgs a, PipeWs
   if (col == 0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (2 * j + g < wave_rows) w.cnt[Lg * kTileRows + 8 * wv + 2 * j + g] = (uint32_t)cnt[j];
+      if (2 * j + g < wave_rows)
+        w.cnt[Lg * kTileRows + 8 * wv + 2 * j + g] = (uint32_t)(g ? cnt_hi[j] : cnt_lo[j]);
   }
 }
 
