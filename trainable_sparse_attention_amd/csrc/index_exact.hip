@@ -102,7 +102,7 @@ __global__ __launch_bounds__(512, 1) void index_exact_kernel(IndexArgs a, uint64
   constexpr int kStageBlk = LDS::kBlk;
   constexpr int kThreads = kWaves * 64;
   const int tid = threadIdx.x;
-  const int wv = tid >> 6, lane = tid & 63, col = lane & 31, g = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, col = lane & 31, g = lane >> 5;
   const uint32_t lt32 = (1u << col) - 1u;
   const int half = a.R / 2;
   // Region A: prologue (rope table + rotated-query scratch) then the stages

@@ -344,7 +344,9 @@ __global__ __launch_bounds__(kCutWaves * 64) void index_cut_kernel(IndexArgs a, 
                                                                     int ntiles, int nrows) {
   __shared__ uint32_t hist[kCutWaves][256];
   __shared__ uint32_t lsc[kCutWaves][kList];
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index as a scalar: the row, its count and its list are then
+  // wave-uniform
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int slot = blockIdx.x * kCutWaves + wv;
   if (slot >= nrows) return;
   const int Lg = slot / kTileRows;

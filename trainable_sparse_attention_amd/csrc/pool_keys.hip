@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(const T* __restrict__ k_
                                                         double log2_theta) {
   __shared__ float mean_s[4][128];
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t job = (int64_t)blockIdx.x * 4 + wv;  // (sequence, block) pair
   const bool live = job < (int64_t)B * nblk;
   const int64_t b = live ? job / nblk : 0, j = live ? b0 + job % nblk : 0;
