@@ -15,15 +15,16 @@
 //   collect : grid (slices, B * n_q).  Every workgroup finds the bin holding
 //             the k_B-th largest score from the global histogram; when the
 //             scores at or above that bin's lower edge fit kCandCap, it
-//             appends its slice's share of them, in block order, to the
-//             token's candidate list (one atomic reservation per slice).
+//             writes its slice's share of them, in block order, to the
+//             slice's own region of the token's candidate area (no atomics);
+//             slice 0 also records the bin and the counts for select.
 //   select  : one workgroup per (sequence, new token).  Gathers the slice
 //             lists in slice order (= block order) and cuts them to the exact
-//             top k_B (score desc, block id asc) with the radix rule shared
-//             with the prefill kernel; writes ascending block ids.  When the
-//             list would not fit (e.g. most scores are zero), it selects from
-//             all scores instead, refining the histogram until the
-//             candidates fit.
+//             top k_B (score desc, block id asc): the bin fixes the top 12
+//             bits, two 10-bit radix passes the rest; writes ascending block
+//             ids.  When the list would not fit (e.g. most scores are zero),
+//             it selects from all scores instead, refining the histogram
+//             until the candidates fit.
 #include "index_common.h"
 
 namespace qsa {
@@ -43,9 +44,9 @@ struct DecodeWs {
   float* qrot;       // [B*n_q][4][128] rotated indexer queries
   float* scores;     // [B*n_q][ld]
   uint32_t* ghist;   // [B*n_q][kBins]
-  uint32_t* gfill;   // [B*n_q] candidates appended so far
+  uint32_t* meta;    // [B*n_q][4]: bin of the k_B-th score, count above it, count >= its edge
   uint32_t* table;   // [B*n_q][nslice][2] (offset, count) of each slice's list
-  uint64_t* cand;    // [B*n_q][kCandCap] (score bits << 32 | block id)
+  uint64_t* cand;    // [B*n_q][nslice][kCandCap] (score bits << 32 | block id)
   int64_t ld;        // score row stride (multiple of 4 floats)
   int nsplit;
   int chunk;         // blocks per scan split (multiple of 64)
@@ -85,9 +86,9 @@ static DecodeWs carve(void* ws, int B, int n_q, int64_t nb_cap, size_t* total) {
   d.qrot = (float*)take(rows * 4 * 128 * sizeof(float));
   d.scores = (float*)take(rows * (size_t)d.ld * sizeof(float));
   d.ghist = (uint32_t*)take(rows * kBins * sizeof(uint32_t));
-  d.gfill = (uint32_t*)take(rows * sizeof(uint32_t));
+  d.meta = (uint32_t*)take(rows * 4 * sizeof(uint32_t));
   d.table = (uint32_t*)take(rows * (size_t)d.nslice * 2 * sizeof(uint32_t));
-  d.cand = (uint64_t*)take(rows * kCandCap * sizeof(uint64_t));
+  d.cand = (uint64_t*)take(rows * (size_t)d.nslice * kCandCap * sizeof(uint64_t));
   if (total) *total = off;
   return d;
 }
@@ -107,7 +108,7 @@ __device__ __forceinline__ int64_t dec_nb(const IndexArgs& a, int b, int t) {
 }
 
 // Rotate the 4 indexer heads of one new token (RoPE at its position on the
-// first R dims, rotate-half pairs) and clear its histogram and list counter.
+// first R dims, rotate-half pairs) and clear its histogram.
 template <typename T>
 __global__ __launch_bounds__(256) void index_decode_prep(IndexArgs a, DecodeWs w) {
   __shared__ float2 table[64];
@@ -132,7 +133,6 @@ __global__ __launch_bounds__(256) void index_decode_prep(IndexArgs a, DecodeWs w
   }
   uint32_t* h = w.ghist + (int64_t)row * kBins;
   for (int e = tid; e < kBins; e += 256) h[e] = 0;
-  if (tid == 0) w.gfill[row] = 0;
   __syncthreads();
   float* dst = w.qrot + (int64_t)row * 4 * 128;
 #pragma unroll
@@ -287,7 +287,6 @@ __global__ __launch_bounds__(kCollectThreads) void index_decode_collect(IndexArg
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t red[2 * NW + 2];
   __shared__ uint32_t wsum[NW];
-  __shared__ uint32_t base_s;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int slice = blockIdx.x, row = blockIdx.y;
   const int b = row / a.n_q, t = row % a.n_q;
@@ -316,7 +315,14 @@ __global__ __launch_bounds__(kCollectThreads) void index_decode_collect(IndexArg
   __syncthreads();
   uint32_t above;
   const int bin = block_find_bin<kCollectThreads>(hist, kBins, (uint32_t)a.kB, red, &above);
-  if (above + hist[bin] > (uint32_t)kCandCap) return;  // select takes the exact route
+  const uint32_t count = above + hist[bin];
+  if (slice == 0 && tid == 0) {
+    uint32_t* m = w.meta + (int64_t)row * 4;
+    m[0] = (uint32_t)bin;
+    m[1] = above;
+    m[2] = count;
+  }
+  if (count > (uint32_t)kCandCap) return;  // select takes the exact route
   const uint32_t thr = (uint32_t)bin << 20;
   uint32_t mask = 0;
 #pragma unroll
@@ -337,16 +343,16 @@ __global__ __launch_bounds__(kCollectThreads) void index_decode_collect(IndexArg
     before += x < wv ? wsum[x] : 0u;
     total += wsum[x];
   }
+  // the slice's share is at most the row's count (<= kCandCap): it has a
+  // region of that size of its own
+  const uint32_t off = (uint32_t)slice * kCandCap;
   if (tid == 0) {
-    const uint32_t off = total ? atomicAdd(&w.gfill[row], total) : 0u;
-    base_s = off;
     uint32_t* te = w.table + ((int64_t)row * w.nslice + slice) * 2;
     te[0] = off;
     te[1] = total;
   }
-  __syncthreads();
-  uint32_t p = base_s + before + incl - mine;
-  uint64_t* dst = w.cand + (int64_t)row * kCandCap;
+  uint32_t p = off + before + incl - mine;
+  uint64_t* dst = w.cand + (int64_t)row * w.nslice * kCandCap;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j)
     if (mask >> j & 1u) dst[p++] = ((uint64_t)bits[j] << 32) | (uint32_t)(e0 + j);
@@ -367,13 +373,16 @@ __global__ __launch_bounds__(kSelThreads) void index_decode_select(IndexArgs a, 
     return;
   }
   const uint32_t k = (uint32_t)a.kB;
-  const uint32_t* gh = w.ghist + (int64_t)row * kBins;
-  for (int e = tid; e < kBins; e += kSelThreads) hist[e] = gh[e];
-  __syncthreads();
-  uint32_t above;
-  int bin = block_find_bin<kSelThreads>(hist, kBins, k, red, &above);
-  uint32_t count = above + hist[bin];
+  // bin of the k-th score, entries in larger bins, entries >= its lower edge
+  const uint32_t* mrow = w.meta + (int64_t)row * 4;
+  const int bin = (int)mrow[0];
+  uint32_t above = mrow[1];
+  uint32_t count = mrow[2];
   int c;
+  // radix cut of the collected list: the first pass resolves the bits below
+  // `resolved` (the list's entries all share or exceed `cut_prefix` there)
+  uint32_t cut_prefix = 0, cut_mask = 0, cut_krem = k;
+  int cut_bits = 8;
   if (count <= (uint32_t)kCandCap && w.nslice <= kMaxSlicesFast) {
     // fast route: the collect kernel left every score >= bin << 20 in
     // per-slice lists; place them in slice order
@@ -396,7 +405,8 @@ __global__ __launch_bounds__(kSelThreads) void index_decode_select(IndexArgs a, 
     if (tid < w.nslice) spos[tid] = before + incl - mine;
     __syncthreads();
     c = (int)count;
-    const uint64_t* src = w.cand + (int64_t)row * kCandCap;
+    const uint64_t* src = w.cand + (int64_t)row * w.nslice * kCandCap;
+    const uint32_t lim = (uint32_t)w.nslice * kCandCap - 1;
     for (int pidx = tid; pidx < c; pidx += kSelThreads) {
       // slice holding list position pidx: the last s with spos[s] <= pidx
       int lo_s = 0, hi_s = w.nslice - 1;
@@ -406,9 +416,14 @@ __global__ __launch_bounds__(kSelThreads) void index_decode_select(IndexArgs a, 
       }
       // (empty slices share their start with the next slice, so the last
       // such s is never empty)
-      cand[pidx] = src[min(soff[lo_s] + (pidx - spos[lo_s]), (uint32_t)kCandCap - 1)];
+      cand[pidx] = src[min(soff[lo_s] + (pidx - spos[lo_s]), lim)];
     }
     __syncthreads();
+    // every entry is >= the bin's edge; the `above` ones lie in larger bins
+    cut_prefix = (uint32_t)bin << 20;
+    cut_mask = 0xFFF00000u;
+    cut_krem = k - above;
+    cut_bits = 10;
   } else {
     // exact route over all scores: refine the bin while the candidates
     // (>= prefix) do not fit: 12 + 12 + 8 bits
@@ -487,21 +502,22 @@ __global__ __launch_bounds__(kSelThreads) void index_decode_select(IndexArgs a, 
   // workgroup: radix select of the k-th score, then an ordered compaction
   // (every score above it, and the first equal ones up to k)
   __syncthreads();
-  uint32_t prefix = 0, pmask = 0;
-  uint32_t krem = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int e = tid; e < 256; e += kSelThreads) hist[e] = 0;
+  uint32_t prefix = cut_prefix, pmask = cut_mask;
+  uint32_t krem = cut_krem;
+  const int nbin = 1 << cut_bits;
+  for (int shift = 32 - __popc(cut_mask) - cut_bits; shift >= 0; shift -= cut_bits) {
+    for (int e = tid; e < nbin; e += kSelThreads) hist[e] = 0;
     __syncthreads();
     for (int e = tid; e < c; e += kSelThreads) {
       const uint32_t sb = (uint32_t)(cand[e] >> 32);
-      if ((sb & pmask) == prefix) atomicAdd(&hist[(sb >> shift) & 255u], 1u);
+      if ((sb & pmask) == prefix) atomicAdd(&hist[(sb >> shift) & (uint32_t)(nbin - 1)], 1u);
     }
     __syncthreads();
     uint32_t ab;
-    const int digit = block_find_bin<kSelThreads>(hist, 256, krem, red, &ab);
+    const int digit = block_find_bin<kSelThreads>(hist, nbin, krem, red, &ab);
     krem -= ab;
     prefix |= (uint32_t)digit << shift;
-    pmask |= 255u << shift;
+    pmask |= (uint32_t)(nbin - 1) << shift;
     __syncthreads();
   }
   const uint32_t v = prefix;  // the k-th largest score; krem equal ones are kept
