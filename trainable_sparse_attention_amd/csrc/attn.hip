@@ -138,8 +138,10 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
   // Block ids of a window of kIdWin slots from `base` (the tail slot is block
   // nb; slots past the set read block 0 and are masked).
   int base = s0;
+  // (at most the window, and no further than the chunk that holds slot s1 - 1)
+  const int fill_n = min(kIdWin, (s1 - s0 + kSlotsPerChunk - 1) / kSlotsPerChunk * kSlotsPerChunk);
   auto fill_ids = [&](int b0) {
-    for (int u = lane; u < kIdWin; u += 64) {
+    for (int u = lane; u < fill_n; u += 64) {
       const int sl = b0 + u;
       ids[u] = sl < R.cnt ? R.ids[sl] : (sl < s1 ? (int)R.nb : 0);
     }
@@ -492,15 +494,20 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, int nsplit, fl
   }
 }
 
-// Merge split partials: one 128-thread block per (b, t, query head), thread =
-// output dim.  The split weights 2^(m_s - M) are formed once in LDS, then each
-// thread sums its dim over the splits with independent loads in flight.
+// Merge split partials: one workgroup per (b, t, query head) of kCombGroups
+// groups of 128 threads, thread = output dim; group j sums the splits
+// j, j + kCombGroups, ...  Every partial load is issued before the split
+// weights 2^(m_s - M) are known, so the merge waits on one round of loads.
+constexpr int kCombGroups = 4;
+constexpr int kCombUnroll = 17;  // splits per thread kept in registers (65 splits: 17 per group)
 template <typename T>
-__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, int nsplit,
-                                                           const float* __restrict__ part) {
+__global__ __launch_bounds__(128 * kCombGroups) void attn_combine_kernel(
+    AttnArgs a, int nsplit, const float* __restrict__ part) {
+  constexpr int NT = 128 * kCombGroups, NW = NT / 64;
   extern __shared__ float wgt[];  // [nsplit]
-  __shared__ float red[2];
-  const int dim = threadIdx.x, lane = dim & 63, wv = dim >> 6;
+  __shared__ float red[2 * NW];
+  __shared__ float osum[kCombGroups - 1][128];
+  const int tid = threadIdx.x, dim = tid & 127, grp = tid >> 7, lane = tid & 63, wv = tid >> 6;
   int64_t w = blockIdx.x;
   const int h = (int)(w % a.hq);
   w /= a.hq;
@@ -509,37 +516,53 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, int nspli
   const int G = a.hq / a.hkv;
   const int g = h / G, hl = h % G;
   const float* base = part + (((int64_t)b * a.n_q + t) * a.hkv + g) * nsplit * kPartFloats;
+  const float* po = base + 32 + hl * 128 + dim;
+  float ov[kCombUnroll];
+#pragma unroll
+  for (int u = 0; u < kCombUnroll; ++u) {
+    const int sp = grp + kCombGroups * u;
+    ov[u] = sp < nsplit ? po[(int64_t)sp * kPartFloats] : 0.f;
+  }
   float M = -INFINITY;
-  for (int s = dim; s < nsplit; s += 128) M = fmaxf(M, base[(int64_t)s * kPartFloats + hl]);
+  for (int sp = tid; sp < nsplit; sp += NT) M = fmaxf(M, base[(int64_t)sp * kPartFloats + hl]);
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
   if (lane == 0) red[wv] = M;
   __syncthreads();
-  M = fmaxf(red[0], red[1]);
+  M = red[0];
+#pragma unroll
+  for (int x = 1; x < NW; ++x) M = fmaxf(M, red[x]);
   float L = 0.f;
-  for (int s = dim; s < nsplit; s += 128) {
-    const float* pp = base + (int64_t)s * kPartFloats;
+  for (int sp = tid; sp < nsplit; sp += NT) {
+    const float* pp = base + (int64_t)sp * kPartFloats;
     const float ms = pp[hl];
     const float ws = ms == -INFINITY ? 0.f : exp2f(ms - M);
-    wgt[s] = ws;
+    wgt[sp] = ws;
     L += ws * pp[16 + hl];
   }
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) L += __shfl_xor(L, off);
   __syncthreads();
-  if (lane == 0) red[wv] = L;
+  if (lane == 0) red[NW + wv] = L;
   __syncthreads();
-  L = red[0] + red[1];
-  const float* po = base + 32 + hl * 128 + dim;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  int s = 0;
-  for (; s + 8 <= nsplit; s += 8) {
+  L = 0.f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc[u] += wgt[s + u] * po[(int64_t)(s + u) * kPartFloats];
+  for (int x = 0; x < NW; ++x) L += red[NW + x];
+  float acc = 0.f;
+#pragma unroll
+  for (int u = 0; u < kCombUnroll; ++u) {
+    const int sp = grp + kCombGroups * u;
+    if (sp < nsplit) acc += wgt[sp] * ov[u];
   }
-  for (; s < nsplit; ++s) acc[0] += wgt[s] * po[(int64_t)s * kPartFloats];
-  const float tot = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
-  Elt<T>::st((T*)a.out, (((int64_t)b * a.n_q + t) * a.hq + h) * 128 + dim, tot / L);
+  for (int sp = grp + kCombGroups * kCombUnroll; sp < nsplit; sp += kCombGroups)
+    acc += wgt[sp] * po[(int64_t)sp * kPartFloats];
+  if (grp > 0) osum[grp - 1][dim] = acc;
+  __syncthreads();
+  if (grp == 0) {
+#pragma unroll
+    for (int x = 0; x < kCombGroups - 1; ++x) acc += osum[x][dim];
+    Elt<T>::st((T*)a.out, (((int64_t)b * a.n_q + t) * a.hq + h) * 128 + dim, acc / L);
+  }
 }
 
 // LDS the bf16 kernel uses: one V chunk and a window of slot ids.
@@ -632,11 +655,11 @@ hipError_t launch_attn_decode(qsa_dtype dt, const AttnArgs& a, void* ws, hipStre
   if (e != hipSuccess) return e;
   const dim3 cg((unsigned)((int64_t)a.B * a.n_q * a.hq));
   if (dt == QSA_BF16)
-    hipLaunchKernelGGL(attn_combine_kernel<unsigned short>, cg, dim3(128), nsplit * sizeof(float),
-                       st, a, nsplit, (const float*)part);
+    hipLaunchKernelGGL(attn_combine_kernel<unsigned short>, cg, dim3(128 * kCombGroups),
+                       nsplit * sizeof(float), st, a, nsplit, (const float*)part);
   else
-    hipLaunchKernelGGL(attn_combine_kernel<float>, cg, dim3(128), nsplit * sizeof(float), st, a,
-                       nsplit, (const float*)part);
+    hipLaunchKernelGGL(attn_combine_kernel<float>, cg, dim3(128 * kCombGroups),
+                       nsplit * sizeof(float), st, a, nsplit, (const float*)part);
   return hipGetLastError();
 }
 
