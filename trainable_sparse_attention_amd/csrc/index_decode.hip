@@ -159,6 +159,11 @@ __global__ __launch_bounds__(kScanThreads) void index_decode_scan(IndexArgs a, D
   int64_t nbt[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) nbt[t] = t < a.n_q ? dec_nb(a, b, t) : 0;
+  const int64_t nbmax = nbt[a.n_q - 1];
+  const int64_t lo = (int64_t)split * w.chunk;
+  const int64_t hi = min(lo + (int64_t)w.chunk, nbmax);
+  const T* kb = (const T*)a.kbar + (size_t)b * a.nb_cap * 128;
+  if (lo >= hi) return;  // the whole workgroup: nothing to scan, nothing to count
   // A operand rows 4t + h hold the rotated queries (zero for absent tokens);
   // bf16 keeps a low part for the rotated dims (see split_bf16)
   float vals[16 * 128 / kScanThreads];
@@ -166,10 +171,23 @@ __global__ __launch_bounds__(kScanThreads) void index_decode_scan(IndexArgs a, D
   for (int u = 0; u < 16 * 128 / kScanThreads; ++u) {
     const int e = tid + kScanThreads * u;
     const int t = e >> 9;
-    const float val = t < a.n_q ? w.qrot[((int64_t)b * a.n_q) * 512 + e] : 0.f;
-    vals[u] = val;
-    Elt<T>::st(qs, e, val);
+    vals[u] = t < a.n_q ? w.qrot[((int64_t)b * a.n_q) * 512 + e] : 0.f;
   }
+  // wave wv takes the 16-block tiles lo + 16 (wv + 4 j); the tiles of the
+  // next two steps are in flight while one is scored.  The first two are
+  // issued while the queries are staged (after the query loads, so staging
+  // waits on those alone), unconditionally: the block index is clamped to
+  // the last visible block (nbmax > lo >= 0), so a wave past `hi` reads a
+  // valid row it never scores.
+  auto load = [&](int64_t c0, typename M::Frag* f) {
+    M::load_glb(kb + min(c0 + hl, nbmax - 1) * 128, gq, f);
+  };
+  typename M::Frag B0[M::kCalls], B1[M::kCalls], B2[M::kCalls];
+  int64_t c0 = lo + 16 * wv;
+  load(c0, B0);
+  load(c0 + 64, B1);
+#pragma unroll
+  for (int u = 0; u < 16 * 128 / kScanThreads; ++u) Elt<T>::st(qs, tid + kScanThreads * u, vals[u]);
   __syncthreads();
   typename M::Frag A[M::kCalls];
   typename M::Frag Alo[M::kSplit ? M::kCalls : 1];
@@ -183,19 +201,10 @@ __global__ __launch_bounds__(kScanThreads) void index_decode_scan(IndexArgs a, D
     M::load_lds(qs, 128, hl, gq, Alo);
   }
 
-  const int64_t nbmax = nbt[a.n_q - 1];
-  const int64_t lo = (int64_t)split * w.chunk;
-  const int64_t hi = min(lo + (int64_t)w.chunk, nbmax);
-  const T* kb = (const T*)a.kbar + (size_t)b * a.nb_cap * 128;
   const int tq = gq < a.n_q ? gq : 0;
   const int64_t my_nb = gq < a.n_q ? nbt[gq] : 0;
   float* srow = w.scores + ((int64_t)b * a.n_q + tq) * w.ld;
   uint32_t* my_hist = hist + tq * kBins;
-  // wave wv takes the 16-block tiles lo + 16 (wv + 4 j); the tiles of the
-  // next two steps are in flight while one is scored
-  auto load = [&](int64_t c0, typename M::Frag* f) {
-    M::load_glb(kb + min(c0 + hl, nbmax - 1) * 128, gq, f);
-  };
   auto score = [&](int64_t c0, const typename M::Frag* f) {
     const float sc = relu_sum4(M::template dot<NLO>(A, Alo, f));
     const int64_t blk = c0 + hl;
@@ -204,10 +213,6 @@ __global__ __launch_bounds__(kScanThreads) void index_decode_scan(IndexArgs a, D
       atomicAdd(&my_hist[__float_as_uint(sc) >> 20], 1u);
     }
   };
-  typename M::Frag B0[M::kCalls], B1[M::kCalls], B2[M::kCalls];
-  int64_t c0 = lo + 16 * wv;
-  if (c0 < hi) load(c0, B0);
-  if (c0 + 64 < hi) load(c0 + 64, B1);
   for (; c0 < hi; c0 += 192) {
     if (c0 + 128 < hi) load(c0 + 128, B2);
     score(c0, B0);
