@@ -377,12 +377,14 @@ template <> struct Mma32<float> {
 // Radix select, 8 bits per pass, starting below the leading bits all entries
 // share (so the first digit already spreads the entries over the bins).
 // `hist` is 256 words of LDS private to the wave.
-template <typename Get>
-__device__ __forceinline__ void wave_radix_kth(Get get, int c, int k, uint32_t* hist, int lane,
-                                               uint32_t* v_out, int* krem_out) {
-  const uint32_t s0 = get(0);
+// The entries are visited through each(f), which calls f(score bits) for
+// every entry the calling lane owns (each entry owned by exactly one lane);
+// s0 is any one entry's score.
+template <typename Each>
+__device__ __forceinline__ void wave_radix_kth_each(Each each, uint32_t s0, int k, uint32_t* hist,
+                                                    int lane, uint32_t* v_out, int* krem_out) {
   uint32_t diff = 0;
-  for (int e = lane; e < c; e += 64) diff |= get(e) ^ s0;
+  each([&](uint32_t sb) { diff |= sb ^ s0; });
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) diff |= __shfl_xor(diff, off);
   int hi = diff ? 31 - __clz(diff) : -1;  // highest bit that differs
@@ -395,10 +397,9 @@ __device__ __forceinline__ void wave_radix_kth(Get get, int c, int k, uint32_t* 
 #pragma unroll
     for (int i = 0; i < 4; ++i) hist[4 * lane + i] = 0;
     wave_sync();
-    for (int e = lane; e < c; e += 64) {
-      const uint32_t sb = get(e);
+    each([&](uint32_t sb) {
       if ((sb & pmask) == prefix) atomicAdd(&hist[(sb >> shift) & dmask], 1u);
-    }
+    });
     wave_sync();
     // lane L owns bins 4L..4L+3; count of entries in bins above lane L's.
     uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2],
@@ -442,6 +443,34 @@ __device__ __forceinline__ void wave_radix_kth(Get get, int c, int k, uint32_t* 
   }
   *v_out = prefix;
   *krem_out = krem;
+}
+
+// The same over entries e < c read through get(e); lane L owns e = L + 64 j.
+template <typename Get>
+__device__ __forceinline__ void wave_radix_kth(Get get, int c, int k, uint32_t* hist, int lane,
+                                               uint32_t* v_out, int* krem_out) {
+  wave_radix_kth_each(
+      [&](auto f) {
+        for (int e = lane; e < c; e += 64) f(get(e));
+      },
+      get(0), k, hist, lane, v_out, krem_out);
+}
+
+// The same over scores held in registers: lane L holds entry L + 64 j in
+// sc[j] (c is wave-uniform), so no pass reads memory for them.
+template <int J>
+__device__ __forceinline__ void wave_radix_kth_regs(const uint32_t (&sc)[J], int c, int k,
+                                                    uint32_t* hist, int lane, uint32_t* v_out,
+                                                    int* krem_out) {
+  wave_radix_kth_each(
+      [&](auto f) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+          if (64 * j >= c) break;
+          if (lane + 64 * j < c) f(sc[j]);
+        }
+      },
+      (uint32_t)__shfl((int)sc[0], 0), k, hist, lane, v_out, krem_out);
 }
 
 // Wave-wide, order-preserving: keep the top-k entries (per wave_radix_kth)

@@ -343,7 +343,6 @@ __global__ __launch_bounds__(1024, 1) void index_scan_kernel(IndexArgs a, PipeWs
 __global__ __launch_bounds__(kCutWaves * 64) void index_cut_kernel(IndexArgs a, PipeWs w, int g0,
                                                                     int ntiles, int nrows) {
   __shared__ uint32_t hist[kCutWaves][256];
-  __shared__ uint32_t lsc[kCutWaves][kList];
   // the wave index as a scalar: the row, its count and its list are then
   // wave-uniform
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -367,9 +366,8 @@ __global__ __launch_bounds__(kCutWaves * 64) void index_cut_kernel(IndexArgs a, 
   } else if (c == k) {  // everything is kept: copy in order
     for (int e = lane; e < a.kB; e += 64) out[e] = e < c ? (int32_t)(uint32_t)list[e] : -1;
   } else {
-    // One read of the list: lane holds entries lane + 64 j; their scores go
-    // to LDS for the radix select, their block ids stay in registers for the
-    // order-preserving keep pass.
+    // One read of the list: lane holds entries lane + 64 j in registers, for
+    // the radix select (scores) and the order-preserving keep pass.
     constexpr int J = kList / 64;
     uint32_t klo[J], khi[J];
 #pragma unroll
@@ -379,15 +377,9 @@ __global__ __launch_bounds__(kCutWaves * 64) void index_cut_kernel(IndexArgs a, 
       klo[j] = (uint32_t)key;
       khi[j] = (uint32_t)(key >> 32);
     }
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int e = lane + 64 * j;
-      if (e < c) lsc[wv][e] = khi[j];
-    }
-    wave_sync();
     uint32_t v;
     int krem;
-    wave_radix_kth([&](int e) { return lsc[wv][e]; }, c, k, hist[wv], lane, &v, &krem);
+    wave_radix_kth_regs(khi, c, k, hist[wv], lane, &v, &krem);
     // the top k in block order: every score above v, then the first krem
     // scores equal to v (smaller block ids win ties)
     const uint64_t lt = lanemask_lt(lane);
