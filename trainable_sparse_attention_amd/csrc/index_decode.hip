@@ -176,11 +176,13 @@ __global__ __launch_bounds__(kScanThreads) void index_decode_scan(IndexArgs a, D
   // wave wv takes the 16-block tiles lo + 16 (wv + 4 j); the tiles of the
   // next two steps are in flight while one is scored.  The first two are
   // issued while the queries are staged (after the query loads, so staging
-  // waits on those alone), unconditionally: the block index is clamped to
-  // the last visible block (nbmax > lo >= 0), so a wave past `hi` reads a
-  // valid row it never scores.
+  // waits on those alone).  Every tile load is unconditional: the block
+  // index is clamped to the workgroup's last block (hi > lo >= 0), so a
+  // load past `hi` re-reads a row the workgroup already fetched (a cache
+  // hit) and is never scored, and the compiler's load counts stay exact
+  // (a load inside a branch makes it wait for every load in flight).
   auto load = [&](int64_t c0, typename M::Frag* f) {
-    M::load_glb(kb + min(c0 + hl, nbmax - 1) * 128, gq, f);
+    M::load_glb(kb + min(c0 + hl, hi - 1) * 128, gq, f);
   };
   typename M::Frag B0[M::kCalls], B1[M::kCalls], B2[M::kCalls];
   int64_t c0 = lo + 16 * wv;
@@ -214,13 +216,13 @@ __global__ __launch_bounds__(kScanThreads) void index_decode_scan(IndexArgs a, D
     }
   };
   for (; c0 < hi; c0 += 192) {
-    if (c0 + 128 < hi) load(c0 + 128, B2);
+    load(c0 + 128, B2);
     score(c0, B0);
     if (c0 + 64 >= hi) break;
-    if (c0 + 192 < hi) load(c0 + 192, B0);
+    load(c0 + 192, B0);
     score(c0 + 64, B1);
     if (c0 + 128 >= hi) break;
-    if (c0 + 256 < hi) load(c0 + 256, B1);
+    load(c0 + 256, B1);
     score(c0 + 128, B2);
   }
   __syncthreads();
