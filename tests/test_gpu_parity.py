@@ -225,15 +225,20 @@ def test_bf16_medium_end_to_end_and_chunking():
         assert blk in set(g_idx[b, i, :g_cnt[b, i]].tolist())
 
 
-@pytest.mark.parametrize("n_q,dtype", [(1, "bf16"), (4, "bf16"), (1, "fp32"), (6, "bf16")])
-def test_decode_parity(n_q, dtype):
+@pytest.mark.parametrize("n_q,dtype,K,lens", [
+    (1, "bf16", 2048, (9000, 9001, 5003)), (4, "bf16", 2048, (9000, 9001, 5003)),
+    (1, "fp32", 2048, (9000, 9001, 5003)), (6, "bf16", 2048, (9000, 9001, 5003)),
+    # short sequences (at most 64 pooled blocks: one 16-block tile per scan
+    # wave) with k_B = 16, so most rows still select
+    (1, "bf16", 64, (256, 201, 90)), (4, "bf16", 64, (256, 201, 90))])
+def test_decode_parity(n_q, dtype, K, lens):
     """Ragged sequence lengths; n_q new tokens per sequence (4 = the pages'
     next_n); decode equals the prefill rows at the same positions."""
-    say("decode n_q=%d %s" % (n_q, dtype))
-    lens = [9000, 9001, 5003]
+    say("decode n_q=%d %s K=%d lens=%s" % (n_q, dtype, K, lens))
+    lens = list(lens)
     n = max(lens)
     d = inputs.small(B=3, n=n, hq=16, hkv=2, dtype=dtype, seed=40 + n_q)
-    p = _params()
+    p = _params(K=K)
     t = _dev_inputs(d)
     nbc = n // 4
     kbar = _pool_gpu(p, t["k_idx"], nbc)
@@ -252,7 +257,7 @@ def test_decode_parity(n_q, dtype):
     for b, L in enumerate(lens):
         rows = np.arange(L - n_q, L)
         assert np.array_equal(g_idx[b], p_idx[b][rows]) and np.array_equal(g_cnt[b], p_cnt[b][rows])
-        o_idx, o_cnt = oracle.index_rows(d["q_idx"][b], kbar_h[b], rows)
+        o_idx, o_cnt = oracle.index_rows(d["q_idx"][b], kbar_h[b], rows, K=K)
         sc = oracle.score_rows(d["q_idx"][b], kbar_h[b], rows)
         check_sets(g_idx[b], g_cnt[b], o_idx, o_cnt, sc)
         o = oracle.attend_rows(d["q"][b], d["k"][b], d["v"][b], rows, g_idx[b], g_cnt[b])

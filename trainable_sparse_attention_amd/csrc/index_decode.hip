@@ -54,14 +54,15 @@ struct DecodeWs {
 };
 
 static int decode_nsplit(int B, int64_t nb_cap, int* chunk_out) {
-  // ~8 workgroups per CU over the whole batch, at least 256 blocks each.
+  // ~8 workgroups per CU over the whole batch, at least 256 blocks each; a
+  // split is 64, 256 or 1024 blocks (1, 4 or 16 tiles of 16 blocks per wave,
+  // a compile-time count, so the tile loop is straight-line code)
   int64_t want = (2048 + B - 1) / B;
   int64_t maxs = (nb_cap + 255) / 256;
   if (want > maxs) want = maxs;
   if (want < 1) want = 1;
   int64_t chunk = (nb_cap + want - 1) / want;
-  chunk = (chunk + 63) & ~(int64_t)63;
-  if (chunk < 64) chunk = 64;
+  chunk = chunk <= 64 ? 64 : (chunk <= 256 ? 256 : 1024);
   const int64_t ns = (nb_cap + chunk - 1) / chunk;
   *chunk_out = (int)chunk;
   return (int)(ns < 1 ? 1 : ns);
@@ -147,13 +148,16 @@ __global__ __launch_bounds__(256) void index_decode_prep(IndexArgs a, DecodeWs w
   }
 }
 
-template <typename T, int NLO>
+// TPW: 16-block tiles per wave (the split holds 4 * 16 * TPW blocks).
+template <typename T, int NLO, int TPW>
 __global__ __launch_bounds__(kScanThreads) void index_decode_scan(IndexArgs a, DecodeWs w) {
   typedef Mma<T> M;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_dec[];
   T* qs = (T*)smem_dec;                                           // [16][128]
   uint32_t* hist = (uint32_t*)(smem_dec + 16 * 128 * sizeof(T));  // [n_q][kBins]
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, hl = lane & 15, gq = lane >> 4;
+  // the wave index as a scalar: tile positions are wave-uniform
+  const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63,
+            hl = lane & 15, gq = lane >> 4;
   const int split = blockIdx.x, b = blockIdx.y;
   for (int e = tid; e < a.n_q * kBins; e += kScanThreads) hist[e] = 0;
   int64_t nbt[4];
@@ -173,21 +177,22 @@ __global__ __launch_bounds__(kScanThreads) void index_decode_scan(IndexArgs a, D
     const int t = e >> 9;
     vals[u] = t < a.n_q ? w.qrot[((int64_t)b * a.n_q) * 512 + e] : 0.f;
   }
-  // wave wv takes the 16-block tiles lo + 16 (wv + 4 j); the tiles of the
-  // next two steps are in flight while one is scored.  The first two are
-  // issued while the queries are staged (after the query loads, so staging
-  // waits on those alone).  Every tile load is unconditional: the block
-  // index is clamped to the workgroup's last block (hi > lo >= 0), so a
-  // load past `hi` re-reads a row the workgroup already fetched (a cache
-  // hit) and is never scored, and the compiler's load counts stay exact
-  // (a load inside a branch makes it wait for every load in flight).
+  // Wave wv takes the TPW 16-block tiles lo + 16 (wv + 4 j), j < TPW, in
+  // three rotating buffers: the next two tiles are in flight while one is
+  // scored.  The first three are issued while the queries are staged (after
+  // the query loads, so staging waits on those alone).  The tile loop is
+  // unrolled and every load is unconditional: the block index is clamped to
+  // the workgroup's last block (hi > lo >= 0), so a tile past `hi` re-reads
+  // rows the workgroup already fetched (cache hits) and is never scored, and
+  // the compiler's load counts stay exact (a load inside a branch or a loop
+  // makes it wait for every load in flight).
   auto load = [&](int64_t c0, typename M::Frag* f) {
     M::load_glb(kb + min(c0 + hl, hi - 1) * 128, gq, f);
   };
-  typename M::Frag B0[M::kCalls], B1[M::kCalls], B2[M::kCalls];
-  int64_t c0 = lo + 16 * wv;
-  load(c0, B0);
-  load(c0 + 64, B1);
+  typename M::Frag Bt[3][M::kCalls];
+  const int64_t c00 = lo + 16 * wv;
+#pragma unroll
+  for (int j = 0; j < 3 && j < TPW; ++j) load(c00 + 64 * j, Bt[j]);
 #pragma unroll
   for (int u = 0; u < 16 * 128 / kScanThreads; ++u) Elt<T>::st(qs, tid + kScanThreads * u, vals[u]);
   __syncthreads();
@@ -215,15 +220,10 @@ __global__ __launch_bounds__(kScanThreads) void index_decode_scan(IndexArgs a, D
       atomicAdd(&my_hist[__float_as_uint(sc) >> 20], 1u);
     }
   };
-  for (; c0 < hi; c0 += 192) {
-    load(c0 + 128, B2);
-    score(c0, B0);
-    if (c0 + 64 >= hi) break;
-    load(c0 + 192, B0);
-    score(c0 + 64, B1);
-    if (c0 + 128 >= hi) break;
-    load(c0 + 256, B1);
-    score(c0 + 128, B2);
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    score(c00 + 64 * j, Bt[j % 3]);
+    if (j + 3 < TPW) load(c00 + 64 * (j + 3), Bt[j % 3]);
   }
   __syncthreads();
   for (int e = tid; e < a.n_q * kBins; e += kScanThreads) {
@@ -562,6 +562,32 @@ __global__ __launch_bounds__(kSelThreads) void index_decode_select(IndexArgs a, 
   if (tid == 0) a.cnt[row] = (int)k;
 }
 
+template <int TPW>
+static hipError_t launch_scan_tpw(qsa_dtype dt, const IndexArgs& a, const DecodeWs& w, dim3 g1,
+                                  size_t lds, hipStream_t st) {
+  if (dt != QSA_BF16)
+    hipLaunchKernelGGL((index_decode_scan<float, 0, TPW>), g1, dim3(kScanThreads), lds, st, a, w);
+  else if (a.R == 0)
+    hipLaunchKernelGGL((index_decode_scan<unsigned short, 0, TPW>), g1, dim3(kScanThreads), lds,
+                       st, a, w);
+  else if (a.R <= 64)
+    hipLaunchKernelGGL((index_decode_scan<unsigned short, 2, TPW>), g1, dim3(kScanThreads), lds,
+                       st, a, w);
+  else
+    hipLaunchKernelGGL((index_decode_scan<unsigned short, 4, TPW>), g1, dim3(kScanThreads), lds,
+                       st, a, w);
+  return hipGetLastError();
+}
+
+static hipError_t launch_scan(qsa_dtype dt, const IndexArgs& a, const DecodeWs& w, dim3 g1,
+                              size_t lds, hipStream_t st) {
+  switch (w.chunk) {
+    case 64: return launch_scan_tpw<1>(dt, a, w, g1, lds, st);
+    case 256: return launch_scan_tpw<4>(dt, a, w, g1, lds, st);
+    default: return launch_scan_tpw<16>(dt, a, w, g1, lds, st);
+  }
+}
+
 hipError_t launch_index_decode(qsa_dtype dt, const IndexArgs& a, void* ws, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
   const DecodeWs w = carve(ws, a.B, a.n_q, a.nb_cap, nullptr);
@@ -575,17 +601,7 @@ hipError_t launch_index_decode(qsa_dtype dt, const IndexArgs& a, void* ws, hipSt
   const dim3 g1((unsigned)w.nsplit, (unsigned)a.B);
   const size_t lds_bf = 16 * 128 * 2 + (size_t)a.n_q * kBins * 4;
   const size_t lds_f = 16 * 128 * 4 + (size_t)a.n_q * kBins * 4;
-  if (dt != QSA_BF16)
-    hipLaunchKernelGGL((index_decode_scan<float, 0>), g1, dim3(kScanThreads), lds_f, st, a, w);
-  else if (a.R == 0)
-    hipLaunchKernelGGL((index_decode_scan<unsigned short, 0>), g1, dim3(kScanThreads), lds_bf, st,
-                       a, w);
-  else if (a.R <= 64)
-    hipLaunchKernelGGL((index_decode_scan<unsigned short, 2>), g1, dim3(kScanThreads), lds_bf, st,
-                       a, w);
-  else
-    hipLaunchKernelGGL((index_decode_scan<unsigned short, 4>), g1, dim3(kScanThreads), lds_bf, st,
-                       a, w);
+  if ((e = launch_scan(dt, a, w, g1, dt == QSA_BF16 ? lds_bf : lds_f, st)) != hipSuccess) return e;
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(index_decode_collect, dim3((unsigned)w.nslice, rows), dim3(kCollectThreads),
                      0, st, a, w);
