@@ -7,18 +7,27 @@ attention; bf16, 16 query / 2 KV heads, K = 2048, r = 4), with every input
 resident in HBM before the timed region.  `value` is prefill tokens/s.  The
 decode half of the metric (batch 8, 1,048,576 cached tokens each, one new
 token per sequence: pool the new block -> indexer + top-k -> split attention)
-is timed the same way and reported under "decode".
+is timed the same way and reported under "decode"; further decode workloads
+(batch 64 at 256K; batch 4 at 1M with 4 new tokens per step, the pages'
+setting) under "decode_more".
 
-Stage times come from HIP events recorded on the stream the kernels run on
-(torch's current stream).  The roofline object describes the stage that
-takes the most time.  The CPU oracle is timed on a bounded uniform sample of
-the same workload's rows on this host (cpu_baseline).
+Timing: HIP events recorded on the stream the kernels run on (torch's current
+stream) around every step and stage.  Before each timed step an untimed
+512 MB fill evicts L2 and the memory-side cache, so every step starts cold;
+the same steps back to back without it are reported under "unflushed".  GPU
+clocks are read before and after the timed region.
+
+The roofline object describes the kernel that takes the most time (the
+prefill attention) against the bf16 MFMA peak with its algorithmic FLOPs; its
+gathers are placed against a measured ceiling: a memory-only replay of the
+same gathers (include/qsa_probe.h), swept over waves per CU and chunks in
+flight.  The CPU oracle is timed on a bounded uniform sample of the same
+workload's rows on this host (cpu_baseline).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -29,6 +38,7 @@ sys.path.insert(0, ROOT)
 METRIC = "QSA prefill tokens/s @256K and decode tokens/s @1M ctx, 1 MI355X; % roofline"
 PEAK_BF16_TFLOPS = 2500.0   # dense bf16 MFMA, MI355X
 PEAK_HBM_GBS = 8000.0       # HBM3E, MI355X
+FLUSH_BYTES = 512 << 20
 
 
 def parse():
@@ -37,9 +47,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--decode-steps", type=int, default=50)
-    ap.add_argument("--prefill-cfg", default="cfg2")
-    ap.add_argument("--decode-cfg", default="cfg4d")
+    ap.add_argument("--prefill-cfg", default="prefill_256k")
+    ap.add_argument("--decode-cfg", default="decode_8x1m")
+    ap.add_argument("--more-decode", default="decode_64x256k,decode_4x1m_next4",
+                    help="comma-separated further decode workloads ('' for none)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=16384,
                     help="uniformly spaced prefill rows the CPU oracle computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -50,10 +64,32 @@ def parse():
     return ap.parse_args()
 
 
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def gpu_clocks():
+    """Current graphics and memory clocks of device 0 (MHz), best effort."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        try:
+            h = amdsmi.amdsmi_get_processor_handles()[0]
+            gfx = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+            mem = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.MEM)
+            return {"gfx_mhz": gfx.get("clk"), "gfx_max_mhz": gfx.get("max_clk"),
+                    "mem_mhz": mem.get("clk")}
+        finally:
+            amdsmi.amdsmi_shut_down()
+    except Exception as e:  # the reading is informative only
+        return {"error": str(e)[:120]}
+
+
 def recorded_traffic(kernel):
-    """HBM bytes per launch of `kernel` recorded from rocprofv3 counter runs in
-    profiles/traffic.txt, if the kernel's source still has the recorded
-    sha256 (else None: the counters describe another version)."""
+    """Bytes per launch of `kernel` from beyond L2 (MALL or HBM) recorded from
+    rocprofv3 counter runs in profiles/traffic.txt, if the kernel's source
+    still has the recorded sha256 (else None: the counters describe another
+    version)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.txt")
     if not os.path.exists(path):
@@ -79,7 +115,43 @@ def sum_nb(n, r=4):
     return r * q * (q - 1) // 2 + q * (rem + 1)
 
 
-def bench_prefill(args, torch, qsa, inputs):
+class Flusher:
+    """An untimed 512 MB fill between timed steps: L2 (4 MB per XCD) and the
+    256 MB memory-side cache then hold none of the step's inputs."""
+
+    def __init__(self, torch, enabled):
+        self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda") if enabled else None
+        self.k = 0
+
+    def __call__(self):
+        if self.buf is not None:
+            self.k = (self.k + 1) & 0xFF
+            self.buf.fill_(self.k)
+
+
+def time_steps(torch, stream, stages, K, flush):
+    """Run K steps (each a list of stage callables) with events around every
+    stage; flush() before each step, outside the events.  Returns
+    (mean step ms, mean ms per stage)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+    st = [0.0] * len(stages)
+    tot = 0.0
+    torch.cuda.synchronize()
+    for _ in range(K):
+        flush()
+        ev[0].record(stream)
+        for i, f in enumerate(stages):
+            f()
+            ev[i + 1].record(stream)
+        ev[-1].synchronize()
+        for i in range(len(stages)):
+            st[i] += ev[i].elapsed_time(ev[i + 1])
+        tot += ev[0].elapsed_time(ev[-1])
+    torch.cuda.synchronize()
+    return tot / K, [s / K for s in st]
+
+
+def bench_prefill(args, torch, qsa, inputs, flush):
     d = inputs.make(args.prefill_cfg, seed=2, backend="torch")
     p = qsa.params()
     B, n, hq, hkv = d["B"], d["n"], d["hq"], d["hkv"]
@@ -93,39 +165,20 @@ def bench_prefill(args, torch, qsa, inputs):
     ws = qsa.workspace(qsa.qsa_index_topk_workspace(p, qsa.dtype_code(d["q_idx"]), B, n, nb,
                                                     False))
     stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-
-    def step(record):
-        if record:
-            ev[0].record(stream)
-        qsa.qsa_pool_keys(p, d["k_idx"], kbar, 0, nb, stream)
-        if record:
-            ev[1].record(stream)
-        qsa.qsa_index_topk(p, d["q_idx"], kbar, idx, cnt, ws, 0, None, stream)
-        if record:
-            ev[2].record(stream)
-        qsa.qsa_sparse_attn_prefill(p, d["q"], d["k"], d["v"], idx, cnt, out, 0, 0.0, stream)
-        if record:
-            ev[3].record(stream)
-
+    stages = [lambda: qsa.qsa_pool_keys(p, d["k_idx"], kbar, 0, nb, stream),
+              lambda: qsa.qsa_index_topk(p, d["q_idx"], kbar, idx, cnt, ws, 0, None, stream),
+              lambda: qsa.qsa_sparse_attn_prefill(p, d["q"], d["k"], d["v"], idx, cnt, out, 0,
+                                                  0.0, stream)]
     for _ in range(args.warmup):
-        step(False)
+        for f in stages:
+            f()
     torch.cuda.synchronize()
-    st = [0.0, 0.0, 0.0]
-    tot = 0.0
+    clk0 = gpu_clocks()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
-        ev[3].synchronize()
-        st[0] += ev[0].elapsed_time(ev[1])
-        st[1] += ev[1].elapsed_time(ev[2])
-        st[2] += ev[2].elapsed_time(ev[3])
-        tot += ev[0].elapsed_time(ev[3])
-    torch.cuda.synchronize()
+    ms, st = time_steps(torch, stream, stages, args.steps, flush)
     wall = time.perf_counter() - t0
-    K = args.steps
-    ms = tot / K
-    st = [s / K for s in st]
+    clk1 = gpu_clocks()
+    ms_u, st_u = time_steps(torch, stream, stages, args.steps, lambda: None)
     # algorithmic work
     pairs = sum_nb(n, p.r) * B
     c = cnt.to(torch.int64)
@@ -134,105 +187,116 @@ def bench_prefill(args, torch, qsa, inputs):
     slots = int(c.sum().item()) * p.r + tails  # sum |T_i|
     elt = 2
     idx_flop = 1024.0 * pairs
-    attn_bytes = (hkv * 2 * 128 * elt * slots + 2 * B * n * hq * 128 * elt +
-                  4 * int(c.sum().item()) + 4 * B * n)
+    attn_flop = 4.0 * 128 * hq * slots
+    gather_bytes = hkv * 2 * 128 * elt * slots
+    attn_bytes = gather_bytes + 2 * B * n * hq * 128 * elt + 4 * int(c.sum().item()) + 4 * B * n
     pool_bytes = B * (n * 128 * elt + nb * 128 * elt)
-    res = dict(n=n, B=B, ms=ms, wall_ms=wall * 1000 / K, stage_ms=st, pairs=pairs, slots=slots,
-               idx_tflops=idx_flop / (st[1] * 1e-3) / 1e12,
-               attn_gbs=attn_bytes / (st[2] * 1e-3) / 1e9,
-               pool_gbs=pool_bytes / (st[0] * 1e-3) / 1e9,
-               idx_flop=idx_flop, attn_bytes=attn_bytes, pool_bytes=pool_bytes,
-               tok_s=B * n / (ms * 1e-3))
-    return res, d
+    res = dict(n=n, B=B, ms=ms, wall_ms=wall * 1000 / args.steps, stage_ms=st, pairs=pairs,
+               slots=slots, idx_flop=idx_flop, attn_flop=attn_flop, attn_bytes=attn_bytes,
+               gather_bytes=gather_bytes, pool_bytes=pool_bytes, tok_s=B * n / (ms * 1e-3),
+               ms_unflushed=ms_u, stage_ms_unflushed=st_u, clocks=[clk0, clk1])
+    probe = None
+    if not args.no_probe:
+        probe = probe_sweep(torch, qsa, p, d, idx, cnt, flush, stream)
+    return res, d, probe
 
 
-def bench_decode(args, torch, qsa, inputs):
-    d = inputs.make(args.decode_cfg, seed=4, backend="torch")
+def probe_sweep(torch, qsa, p, d, idx, cnt, flush, stream):
+    """Memory-only replay of the attention's gathers over waves per CU and
+    chunks in flight per wave; each point is the best of two cold runs."""
+    B, n, hkv = d["B"], d["n"], d["hkv"]
+    sink = torch.empty(B * n * hkv, dtype=torch.int32, device="cuda")
+    pts = []
+    for w, depth in [(8, 1), (8, 2), (8, 4), (12, 2), (16, 1), (16, 2), (16, 4), (0, 4)]:
+        best = None
+        for _ in range(2):
+            ms, _ = time_steps(torch, stream, [lambda: qsa.qsa_probe_gather(
+                p, d["k"], d["v"], idx, cnt, sink, w, depth, 0, stream)], 1, flush)
+            best = ms if best is None else min(best, ms)
+        pts.append({"waves_per_cu": w, "depth": depth, "ms": best})
+        log("gather probe: %s waves/CU, depth %d: %.3f ms" % (w or "max", depth, best))
+    return pts
+
+
+def bench_decode(name, args, torch, qsa, inputs, flush):
+    d = inputs.make(name, seed=4, backend="torch")
     p = qsa.params()
-    B, L, hq, hkv = d["B"], d["n"], d["hq"], d["hkv"]
+    B, L, n_q, hq, hkv = d["B"], d["n"], d["n_q"], d["hq"], d["hkv"]
     kB = qsa.k_blocks(p)
     nb = L // p.r
     dev = d["q"].device
     kbar = torch.empty((B, nb, 128), dtype=d["k_idx"].dtype, device=dev)
     qsa.qsa_pool_keys(p, d["k_idx"], kbar, 0, nb)
     seq_len = torch.full((B,), L, dtype=torch.int32, device=dev)
-    idx = torch.empty((B, 1, kB), dtype=torch.int32, device=dev)
-    cnt = torch.empty((B, 1), dtype=torch.int32, device=dev)
+    idx = torch.empty((B, n_q, kB), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, n_q), dtype=torch.int32, device=dev)
     out = torch.empty_like(d["q"])
-    ws_i = qsa.workspace(qsa.qsa_index_topk_workspace(p, qsa.dtype_code(d["q_idx"]), B, 1, nb,
+    ws_i = qsa.workspace(qsa.qsa_index_topk_workspace(p, qsa.dtype_code(d["q_idx"]), B, n_q, nb,
                                                       True))
-    ws_a = qsa.workspace(qsa.qsa_sparse_attn_decode_workspace(p, B, 1, hq, hkv))
+    ws_a = qsa.workspace(qsa.qsa_sparse_attn_decode_workspace(p, B, n_q, hq, hkv))
     stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-
-    def step(record):
-        if record:
-            ev[0].record(stream)
-        # the newest block completes at this step: pool it into the cache
-        # (calls go to the current stream: the capture stream under a graph)
-        qsa.qsa_pool_keys(p, d["k_idx"], kbar, nb - 1, nb)
-        if record:
-            ev[1].record(stream)
-        qsa.qsa_index_topk(p, d["q_idx"], kbar, idx, cnt, ws_i, 0, seq_len)
-        if record:
-            ev[2].record(stream)
-        qsa.qsa_sparse_attn_decode(p, d["q"], d["k"], d["v"], seq_len, idx, cnt, out, ws_a, 0.0)
-        if record:
-            ev[3].record(stream)
-
+    # the blocks the new tokens complete are pooled into the cache
+    b0, b1 = (L - n_q) // p.r, L // p.r
+    # calls go to the current stream: the capture stream under a graph
+    stages = [lambda: qsa.qsa_pool_keys(p, d["k_idx"], kbar, b0, b1),
+              lambda: qsa.qsa_index_topk(p, d["q_idx"], kbar, idx, cnt, ws_i, 0, seq_len),
+              lambda: qsa.qsa_sparse_attn_decode(p, d["q"], d["k"], d["v"], seq_len, idx, cnt,
+                                                 out, ws_a, 0.0)]
     for _ in range(args.warmup):
-        step(False)
+        for f in stages:
+            f()
     torch.cuda.synchronize()
     K = args.decode_steps
-    st = [0.0, 0.0, 0.0]
-    tot = 0.0
-    for _ in range(K):
-        step(True)
-        ev[3].synchronize()
-        st[0] += ev[0].elapsed_time(ev[1])
-        st[1] += ev[1].elapsed_time(ev[2])
-        st[2] += ev[2].elapsed_time(ev[3])
-        tot += ev[0].elapsed_time(ev[3])
-    eager_ms = tot / K
-    st = [s / K for s in st]
+    eager_ms, st = time_steps(torch, stream, stages, K, flush)
     # The same step captured once in a HIP graph and replayed: one submission
     # per step, so the GPU does not wait for the host between the calls.
     side = torch.cuda.Stream()
     side.wait_stream(stream)
     with torch.cuda.stream(side):
-        step(False)
+        for f in stages:
+            f()
     stream.wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        step(False)
+        for f in stages:
+            f()
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         g.replay()
-    torch.cuda.synchronize()
-    tot = 0.0
-    for _ in range(K):
-        ev[0].record(stream)
-        g.replay()
-        ev[3].record(stream)
-        ev[3].synchronize()
-        tot += ev[0].elapsed_time(ev[3])
-    ms = tot / K
+    ms, _ = time_steps(torch, stream, [g.replay], K, flush)
+    ms_u, _ = time_steps(torch, stream, [g.replay], K, lambda: None)
     c = cnt.to(torch.int64)
-    slots = int(c.sum().item()) * p.r + B * (L % p.r)
+    pos = L - n_q + torch.arange(n_q, device=dev, dtype=torch.int64)
+    tails = int(((pos + 1) % p.r).sum().item()) * B
+    slots = int(c.sum().item()) * p.r + tails
     elt = 2
-    scan_bytes = B * nb * 128 * elt + B * nb * 4  # pooled keys read + one score per block
+    scan_bytes = B * nb * 128 * elt + B * n_q * nb * 4  # pooled keys once + scores
     gather_bytes = hkv * 2 * 128 * elt * slots
-    io_bytes = B * (2 * hq * 128 * elt + 4 * 128 * elt + kB * 4)
+    io_bytes = B * n_q * (2 * hq * 128 * elt + 4 * 128 * elt + kB * 4)
     step_bytes = B * nb * 128 * elt + gather_bytes + io_bytes
-    return dict(B=B, L=L, ms=ms, eager_ms=eager_ms, stage_ms=st, tok_s=B / (ms * 1e-3),
-                step_bytes=step_bytes,
+    return dict(name=name, B=B, L=L, n_q=n_q, ms=ms, ms_unflushed=ms_u, eager_ms=eager_ms,
+                stage_ms=st, tok_s=B * n_q / (ms * 1e-3), step_bytes=step_bytes,
                 scan_bytes=scan_bytes, gather_bytes=gather_bytes,
                 step_gbs=step_bytes / (ms * 1e-3) / 1e9,
                 index_gbs=scan_bytes / (st[1] * 1e-3) / 1e9)
 
 
-def cpu_baseline(args, d, qsa_p):
+def decode_record(inputs, dec, steps):
+    return {
+        "value": dec["tok_s"], "unit": "tokens/s", "ms_per_step": dec["ms"],
+        "steps": steps, "workload": inputs.describe(dec["name"]),
+        "timing": "one HIP graph replay per step (the three calls captured once), "
+                  "512 MB cache flush before each step",
+        "ms_per_step_unflushed": dec["ms_unflushed"],
+        "eager_ms_per_step": dec["eager_ms"],
+        "eager_stage_ms": {"pool_keys": dec["stage_ms"][0], "index_topk": dec["stage_ms"][1],
+                           "sparse_attn_decode": dec["stage_ms"][2]},
+        "step_bytes": dec["step_bytes"], "step_GB/s": dec["step_gbs"],
+        "frac_hbm": dec["step_gbs"] / PEAK_HBM_GBS, "index_GB/s": dec["index_gbs"]}
+
+
+def cpu_baseline(args, d):
     """The oracle on a uniform sample of the prefill rows, extrapolated."""
     import numpy as np
     import oracle
@@ -286,39 +350,52 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-        print("[bench] copy calibration: %d bytes read and %d bytes written per copy" % (
-            nbytes, nbytes), file=sys.stderr, flush=True)
+        log("copy calibration: %d bytes read and %d bytes written per copy" % (nbytes, nbytes))
         del src, dst
         torch.cuda.empty_cache()
-    pre, d = bench_prefill(args, torch, qsa, inputs)
-    print("[bench] prefill %s: %.3f ms/step (pool %.3f, index %.3f, attn %.3f ms)" % (
-        args.prefill_cfg, pre["ms"], *pre["stage_ms"]), file=sys.stderr, flush=True)
+    flush = Flusher(torch, not args.no_flush)
+    pre, d, probe = bench_prefill(args, torch, qsa, inputs, flush)
+    log("prefill %s: %.3f ms/step (pool %.3f, index %.3f, attn %.3f ms); unflushed %.3f ms "
+        "(pool %.3f, index %.3f, attn %.3f ms)" % (args.prefill_cfg, pre["ms"], *pre["stage_ms"],
+                                                   pre["ms_unflushed"],
+                                                   *pre["stage_ms_unflushed"]))
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args, d, qsa.params())
-        print("[bench] cpu baseline %.1f tok/s (%s)" % (cpu["value"], cpu["sample"]),
-              file=sys.stderr, flush=True)
+        cpu = cpu_baseline(args, d)
+        log("cpu baseline %.1f tok/s (%s)" % (cpu["value"], cpu["sample"]))
     del d
     torch.cuda.empty_cache()
-    dec = None
+    decs = []
     if not args.no_decode:
-        dec = bench_decode(args, torch, qsa, inputs)
-        print("[bench] decode %s: %.3f ms/step as a graph replay; eager %.3f ms/step (pool %.3f, "
-              "index %.3f, attn %.3f ms)" % (args.decode_cfg, dec["ms"], dec["eager_ms"],
-                                             *dec["stage_ms"]), file=sys.stderr, flush=True)
+        names = [args.decode_cfg] + [x for x in args.more_decode.split(",") if x]
+        for name in names:
+            dec = bench_decode(name, args, torch, qsa, inputs, flush)
+            log("decode %s: %.4f ms/step as a graph replay (unflushed %.4f); eager %.4f ms/step "
+                "(pool %.4f, index %.4f, attn %.4f ms)" % (name, dec["ms"], dec["ms_unflushed"],
+                                                           dec["eager_ms"], *dec["stage_ms"]))
+            decs.append(dec)
+            torch.cuda.empty_cache()
 
-    names = ["pool_keys", "index_topk", "sparse_attn_prefill"]
-    dom = max(range(3), key=lambda i: pre["stage_ms"][i])
-    if dom == 1:
-        ach = pre["idx_tflops"]
-        roof = dict(bound="mfma", achieved=ach, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=ach / PEAK_BF16_TFLOPS, traffic=None, kernel=names[dom])
-    else:
-        ach = pre["attn_gbs"] if dom == 2 else pre["pool_gbs"]
-        roof = dict(bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=ach / PEAK_HBM_GBS,
-                    traffic=recorded_traffic(names[dom]) if dom == 2 else None,
-                    kernel=names[dom])
+    st = pre["stage_ms"]
+    attn_ms = st[2]
+    attn_tflops = pre["attn_flop"] / (attn_ms * 1e-3) / 1e12
+    gather = {"algorithmic_bytes": pre["gather_bytes"],
+              "achieved_GB/s": pre["gather_bytes"] / (attn_ms * 1e-3) / 1e9,
+              "l2_miss_bytes": recorded_traffic("sparse_attn_prefill")}
+    if probe:
+        best = min(probe, key=lambda x: x["ms"])
+        own = [x for x in probe if x["waves_per_cu"] == 8 and x["depth"] == 1][0]
+        gather.update({"ceiling_ms": best["ms"],
+                       "ceiling_config": {"waves_per_cu": best["waves_per_cu"],
+                                          "depth": best["depth"]},
+                       "ceiling_GB/s": pre["gather_bytes"] / (best["ms"] * 1e-3) / 1e9,
+                       "attn_frac_of_ceiling": best["ms"] / attn_ms,
+                       "probe_at_attn_config_ms": own["ms"], "probe": probe})
+    roof = dict(bound="mfma", achieved=attn_tflops, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                frac=attn_tflops / PEAK_BF16_TFLOPS, traffic=gather["l2_miss_bytes"],
+                kernel="sparse_attn_prefill", flop=pre["attn_flop"],
+                traffic_kind="bytes read and written beyond L2 (served by the memory-side "
+                             "cache or HBM), from rocprofv3 FETCH_SIZE / WRITE_SIZE")
     line = {
         "metric": METRIC,
         "value": pre["tok_s"],
@@ -332,33 +409,34 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "QSA prefill, batch 1, n=262144 tokens, K=2048, r=4, indexer "
-                               "4x128 + 1x128 heads, attention 16 q / 2 kv heads, d=128, bf16",
-                   "global_batch": pre["B"], "seq_len": pre["n"], "parallelism": "none"},
+        "config": {"workload": inputs.describe(args.prefill_cfg), "global_batch": pre["B"],
+                   "seq_len": pre["n"], "parallelism": "none"},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "timing": "HIP events per step on the kernels' stream; 512 MB cache flush before each "
+                  "timed step (not timed)" if not args.no_flush else "HIP events, back to back",
+        "unflushed": {"ms_per_step": pre["ms_unflushed"],
+                      "tokens/s": pre["B"] * pre["n"] / (pre["ms_unflushed"] * 1e-3),
+                      "stage_ms": dict(zip(["pool_keys", "index_topk", "sparse_attn_prefill"],
+                                           pre["stage_ms_unflushed"]))},
+        "clocks": {"before": pre["clocks"][0], "after": pre["clocks"][1]},
         "stages": {
-            "pool_keys": {"ms": pre["stage_ms"][0], "GB/s": pre["pool_gbs"],
-                          "frac_hbm": pre["pool_gbs"] / PEAK_HBM_GBS},
-            "index_topk": {"ms": pre["stage_ms"][1], "TFLOP/s": pre["idx_tflops"],
-                           "frac_mfma": pre["idx_tflops"] / PEAK_BF16_TFLOPS,
-                           "pairs": pre["pairs"]},
-            "sparse_attn_prefill": {"ms": pre["stage_ms"][2], "GB/s": pre["attn_gbs"],
-                                    "frac_hbm": pre["attn_gbs"] / PEAK_HBM_GBS,
-                                    "sum_T": pre["slots"]},
+            "pool_keys": {"ms": st[0], "GB/s": pre["pool_bytes"] / (st[0] * 1e-3) / 1e9,
+                          "frac_hbm": pre["pool_bytes"] / (st[0] * 1e-3) / 1e9 / PEAK_HBM_GBS},
+            "index_topk": {"ms": st[1],
+                           "TFLOP/s": pre["idx_flop"] / (st[1] * 1e-3) / 1e12,
+                           "frac_mfma": pre["idx_flop"] / (st[1] * 1e-3) / 1e12 /
+                           PEAK_BF16_TFLOPS, "pairs": pre["pairs"]},
+            "sparse_attn_prefill": {"ms": attn_ms, "TFLOP/s": attn_tflops,
+                                    "frac_mfma": attn_tflops / PEAK_BF16_TFLOPS,
+                                    "sum_T": pre["slots"], "gather": gather},
         },
     }
-    if dec is not None:
-        line["decode"] = {
-            "value": dec["tok_s"], "unit": "tokens/s", "ms_per_step": dec["ms"],
-            "steps": args.decode_steps,
-            "workload": "QSA decode, batch 8, 1048576 cached tokens per sequence, 1 new token",
-            "timing": "one HIP graph replay per step (the three calls captured once)",
-            "eager_ms_per_step": dec["eager_ms"],
-            "eager_stage_ms": {"pool_keys": dec["stage_ms"][0], "index_topk": dec["stage_ms"][1],
-                               "sparse_attn_decode": dec["stage_ms"][2]},
-            "step_GB/s": dec["step_gbs"], "frac_hbm": dec["step_gbs"] / PEAK_HBM_GBS,
-            "index_GB/s": dec["index_gbs"], "step_bytes": dec["step_bytes"]}
+    if decs:
+        line["decode"] = decode_record(inputs, decs[0], args.decode_steps)
+        if len(decs) > 1:
+            line["decode_more"] = {x["name"]: decode_record(inputs, x, args.decode_steps)
+                                   for x in decs[1:]}
     print(json.dumps(line), flush=True)
 
 

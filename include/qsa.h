@@ -39,8 +39,11 @@
  *   - Inputs must be finite; NaN or Inf give undefined selections.
  *   - Results are deterministic: identical inputs give identical bits.
  *   - Supported shapes: r = 4, h_idx = 4, d_idx = 128, rope_dims even and
- *     <= 128, K >= r, head dim d = 128, hq % hkv == 0, hq / hkv <= 16.
- *     Other values return QSA_ERR_UNSUPPORTED.
+ *     <= 128, K >= r, head dim d = 128, hq % hkv == 0, hq / hkv <= 16;
+ *     k_B = ceil(K/r) <= 3072 for qsa_index_topk over more than 4 query rows
+ *     per sequence and <= 4096 for its decode form (at most 4 new tokens);
+ *     n_cap <= 2^24 tokens for bfloat16 attention.  Other values return
+ *     QSA_ERR_UNSUPPORTED.
  */
 #ifndef QSA_H
 #define QSA_H
@@ -124,7 +127,9 @@ qsa_status qsa_pool_keys(const qsa_params* p, qsa_dtype dtype, const void* k_idx
  *   idx   : [B][n_q][k_B] int32 out;  cnt : [B][n_q] int32 out
  *   workspace : device scratch of qsa_index_topk_workspace(...) bytes
  * Errors: NULL pointers; n_q < 1; a prefill position beyond nb_cap * r
- * -> QSA_ERR_SHAPE; workspace too small -> QSA_ERR_WORKSPACE.  In decode
+ * -> QSA_ERR_SHAPE; workspace too small -> QSA_ERR_WORKSPACE; k_B above
+ * 3072 (more than 4 rows per sequence) or 4096 (decode form) ->
+ * QSA_ERR_UNSUPPORTED.  In decode
  * mode every d_seq_len[b] must lie in [n_q, nb_cap * r] (not checked on the
  * host: the values live on the device).
  */
@@ -150,8 +155,8 @@ size_t qsa_index_topk_workspace(const qsa_params* p, qsa_dtype dtype, int32_t B,
  *   q   : [B][n_q][hq][d];  k, v : [B][hkv][n_cap][d] (head-major caches)
  *   idx, cnt : from qsa_index_topk (same n_q, positions)
  *   out : [B][n_q][hq][d]
- * Errors: NULL pointers; q_pos0 + n_q > n_cap -> QSA_ERR_SHAPE; d != 128 or
- * hq / hkv > 16 -> QSA_ERR_UNSUPPORTED.
+ * Errors: NULL pointers; q_pos0 + n_q > n_cap -> QSA_ERR_SHAPE; d != 128,
+ * hq / hkv > 16, or n_cap > 2^24 with bfloat16 -> QSA_ERR_UNSUPPORTED.
  */
 qsa_status qsa_sparse_attn_prefill(const qsa_params* p, qsa_dtype dtype, const void* q,
                                    const void* k, const void* v, int64_t n_cap,

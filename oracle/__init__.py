@@ -17,4 +17,7 @@ from .oracle import (  # noqa: F401
     attend_rows,
     prefill_rows,
     decode,
+    index_at,
+    score_at,
+    attend_at,
 )

@@ -55,6 +55,12 @@ def load():
         lib.orc_score_rows.restype = None
         lib.orc_attend_rows.argtypes = [P, P, P, I, L, L, P, L, P, P, I, I, I, I, I, D, P]
         lib.orc_attend_rows.restype = None
+        lib.orc_index_at.argtypes = [P, P, I, I, I, I, I, D, I, P, L, P, P]
+        lib.orc_index_at.restype = None
+        lib.orc_score_at.argtypes = [P, P, I, I, I, I, I, D, P, L, P, L]
+        lib.orc_score_at.restype = None
+        lib.orc_attend_at.argtypes = [P, P, P, I, L, P, L, P, P, I, I, I, I, I, D, P]
+        lib.orc_attend_at.restype = None
         _lib = lib
     return _lib
 
@@ -201,3 +207,57 @@ def decode(q_idx_row, q_row, kbar, k, v, seq_len, r=4, K=2048, rope_dims=64, the
     idx, cnt = index_rows(np.asarray(q_idx_row)[None], kbar, [0], pos, r, K, rope_dims, theta)
     out = attend_rows(np.asarray(q_row)[None], k, v, [0], idx, cnt, pos, r, scale)
     return idx[0], int(cnt[0]), out[0]
+
+
+def index_at(q_rows, kbar, pos, r=4, K=2048, rope_dims=64, theta=10000.0):
+    """Selections of query rows given with their positions: q_rows [m][h][d],
+    row u at token position pos[u]; kbar [nb_cap][d].  Returns idx [m][k_B]
+    int32 and cnt [m] int32 (the steps of index_rows)."""
+    q_rows, kbar = _c(q_rows), _c(kbar)
+    dt = _dt(q_rows, kbar)
+    m, h, d = q_rows.shape
+    pos = _c(np.asarray(pos, dtype=np.int64))
+    assert pos.shape == (m,)
+    kB = k_blocks(K, r)
+    if m and kbar.shape[0] < (int(pos.max()) + 1) // r:
+        raise ValueError("kbar too short")
+    idx = np.empty((m, kB), dtype=np.int32)
+    cnt = np.empty(m, dtype=np.int32)
+    load().orc_index_at(_p(q_rows), _p(kbar), dt, h, d, r, rope_dims, float(theta), kB, _p(pos),
+                        m, _p(idx), _p(cnt))
+    return idx, cnt
+
+
+def score_at(q_rows, kbar, pos, r=4, rope_dims=64, theta=10000.0):
+    """Block scores of query rows given with their positions: list of float64
+    arrays, row u of length floor((pos[u] + 1) / r)."""
+    q_rows, kbar = _c(q_rows), _c(kbar)
+    dt = _dt(q_rows, kbar)
+    m, h, d = q_rows.shape
+    pos = _c(np.asarray(pos, dtype=np.int64))
+    stride = max(1, (int(pos.max()) + 1) // r) if m else 1
+    out = np.zeros((m, stride), dtype=np.float64)
+    load().orc_score_at(_p(q_rows), _p(kbar), dt, h, d, r, rope_dims, float(theta), _p(pos), m,
+                        _p(out), stride)
+    return [out[u, : (int(p) + 1) // r] for u, p in enumerate(pos)]
+
+
+def attend_at(q_rows, k, v, pos, idx, cnt, r=4, scale=None):
+    """Attention outputs (float64 [m][hq][D]) of query rows given with their
+    positions and selections.  q_rows [m][hq][D]; k, v [hkv][n_cap][D]."""
+    q_rows, k, v = _c(q_rows), _c(k), _c(v)
+    dt = _dt(q_rows, k, v)
+    m, hq, D = q_rows.shape
+    hkv, n_cap, _ = k.shape
+    pos = _c(np.asarray(pos, dtype=np.int64))
+    idx = _c(np.asarray(idx, dtype=np.int32))
+    cnt = _c(np.asarray(cnt, dtype=np.int32))
+    kB = idx.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if m and int(pos.max()) >= n_cap:
+        raise ValueError("query position beyond the KV capacity")
+    out = np.empty((m, hq, D), dtype=np.float64)
+    load().orc_attend_at(_p(q_rows), _p(k), _p(v), dt, n_cap, _p(pos), m, _p(idx), _p(cnt), kB,
+                         r, hq, hkv, D, float(scale), _p(out))
+    return out

@@ -290,3 +290,43 @@ void orc_attend_rows(const void* q, const void* k, const void* v, int dt, int64_
                out + u * (int64_t)hq * D);
   }
 }
+
+/*
+ * The same three steps for query rows given with explicit positions: row u
+ * of q_rows (h x d indexer values, or hq x D attention values) sits at token
+ * position pos[u].  Used where only a sample of a long sequence's rows is
+ * checked.  OpenMP over rows.
+ */
+void orc_index_at(const void* q_rows, const void* kbar, int dt, int h, int d, int r, int R,
+                  double theta, int kB, const int64_t* pos, int64_t nrows, int32_t* idx,
+                  int32_t* cnt) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t u = 0; u < nrows; ++u) {
+    int64_t nb = orc_nvis(pos[u], r);
+    double* sc = (double*)malloc(sizeof(double) * (size_t)(nb > 0 ? nb : 1));
+    const char* qrow = (const char*)q_rows + (size_t)u * h * d * (dt == ORC_F32 ? 4 : 2);
+    orc_scores(qrow, kbar, dt, h, d, r, R, theta, pos[u], sc);
+    cnt[u] = orc_select(sc, nb, kB, idx + u * kB);
+    free(sc);
+  }
+}
+
+void orc_score_at(const void* q_rows, const void* kbar, int dt, int h, int d, int r, int R,
+                  double theta, const int64_t* pos, int64_t nrows, double* out, int64_t stride) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t u = 0; u < nrows; ++u) {
+    const char* qrow = (const char*)q_rows + (size_t)u * h * d * (dt == ORC_F32 ? 4 : 2);
+    orc_scores(qrow, kbar, dt, h, d, r, R, theta, pos[u], out + u * stride);
+  }
+}
+
+void orc_attend_at(const void* q_rows, const void* k, const void* v, int dt, int64_t n_cap,
+                   const int64_t* pos, int64_t nrows, const int32_t* idx, const int32_t* cnt,
+                   int kB, int r, int hq, int hkv, int D, double scale, double* out) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t u = 0; u < nrows; ++u) {
+    const char* qrow = (const char*)q_rows + (size_t)u * hq * D * (dt == ORC_F32 ? 4 : 2);
+    orc_attend(qrow, k, v, dt, n_cap, pos[u], idx + u * kB, cnt[u], r, hq, hkv, D, scale,
+               out + u * (int64_t)hq * D);
+  }
+}

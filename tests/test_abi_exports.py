@@ -9,14 +9,16 @@ import pytest
 
 from trainable_sparse_attention_amd import qsa
 
-HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
-                   "qsa.h")
+INC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
 
 
 def _declared():
-    src = open(HDR).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(qsa_[a-z_0-9]+)\s*\(", src)))
+    names = set()
+    for f in sorted(os.listdir(INC)):
+        if f.endswith(".h"):
+            src = re.sub(r"/\*.*?\*/", "", open(os.path.join(INC, f)).read(), flags=re.S)
+            names.update(re.findall(r"\b(qsa_[a-z_0-9]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_header_and_binding_agree():
@@ -77,6 +79,34 @@ def test_host_validation_errors():
                                        128, 0.0, fake, fake, 1 << 30, None), 1, lib)
     _expect(lib.qsa_sparse_attn_decode(P, 1, fake, fake, fake, 64, fake, fake, fake, 1, 1, 16, 2,
                                        128, 0.0, fake, fake, 0, None), 5, lib)
+
+
+def test_host_validation_of_built_limits():
+    """Sizes valid for the method but beyond what the kernels are built for
+    are refused on the host: k_B above the candidate-list bounds, and KV
+    capacities whose bf16 byte offsets would not fit 32 bits."""
+    lib = qsa.lib()
+    fake = ctypes.c_void_p(16)
+    big = qsa.params(K=4 * 3073)           # k_B = 3073: many-row lists too small
+    _expect(lib.qsa_index_topk(ctypes.byref(big), 1, fake, fake, 1 << 16, 1, 4096, 0, None,
+                               fake, fake, fake, 1 << 40, None), 4, lib)
+    ok = qsa.params(K=4 * 3072)            # k_B = 3072 passes this check (fails on workspace)
+    _expect(lib.qsa_index_topk(ctypes.byref(ok), 1, fake, fake, 1 << 16, 1, 4096, 0, None,
+                               fake, fake, None, 0, None), 5, lib)
+    dec = qsa.params(K=4 * 4097)           # decode form: k_B = 4097
+    _expect(lib.qsa_index_topk(ctypes.byref(dec), 1, fake, fake, 1 << 16, 2, 1, 0, fake, fake,
+                               fake, fake, 1 << 40, None), 4, lib)
+    p = qsa.params()
+    P = ctypes.byref(p)
+    cap = (1 << 24) + 4
+    _expect(lib.qsa_sparse_attn_prefill(P, 1, fake, fake, fake, cap, fake, fake, 1, 8, 0, 16, 2,
+                                        128, 0.0, fake, None), 4, lib)
+    _expect(lib.qsa_sparse_attn_decode(P, 1, fake, fake, fake, cap, fake, fake, fake, 1, 1, 16,
+                                       2, 128, 0.0, fake, fake, 1 << 30, None), 4, lib)
+    # fp32 addresses rows in 64 bits: the same capacity passes to the
+    # positions check (q_pos0 + n_q beyond n_cap fails instead)
+    _expect(lib.qsa_sparse_attn_prefill(P, 0, fake, fake, fake, cap, fake, fake, 1, 8, cap, 16, 2,
+                                        128, 0.0, fake, None), 2, lib)
 
 
 def test_workspace_sizes_grow_with_work():

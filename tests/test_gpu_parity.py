@@ -70,6 +70,16 @@ def _assert_ids_valid(p, idx, cnt, q_pos0, seq_len):
         assert np.all((np.diff(ids, axis=1) > 0) | ~live[:, 1:]), "index ids not ascending"
 
 
+def _intact_plants(plants):
+    """Planted matches whose keys no later plant of the same sequence
+    overwrote (plants land on uniformly drawn blocks, so two can share one;
+    the later one then holds the block's keys)."""
+    last = {}
+    for u, (b, i, blk, *_r) in enumerate(plants):
+        last[(b, blk)] = u
+    return [pl for u, pl in enumerate(plants) if last[(pl[0], pl[2])] == u]
+
+
 def _attn_gpu(p, q, k, v, idx, cnt, q_pos0=0):
     out = torch.empty_like(q)
     qsa.qsa_sparse_attn_prefill(p, q, k, v, idx, cnt, out, q_pos0)
@@ -118,10 +128,10 @@ def test_pool_parity(dtype):
         assert np.all(got[b, nb:] == 0), "rows beyond the range were written"
 
 
-def test_cfg0_end_to_end_all_rows():
-    """configuration 0 (n=4096, float32, 4 q heads / 1 kv head, 16 planted)."""
-    say("cfg0 end to end")
-    d = inputs.make("cfg0", seed=100)
+def test_prefill_4k_fp32_end_to_end_all_rows():
+    """The 4K-token float32 workload (4 q heads / 1 kv head, 16 planted), every row."""
+    say("4K fp32 end to end")
+    d = inputs.make("prefill_4k_fp32", seed=100)
     p = _params()
     t = _dev_inputs(d)
     kbar = _pool_gpu(p, t["k_idx"], 1024)
@@ -134,12 +144,12 @@ def test_cfg0_end_to_end_all_rows():
     np.testing.assert_allclose(kbar_h[0], ref, rtol=0, atol=4 * 2.0 ** -24 * np.abs(ref).max())
     rows = np.arange(4096)
     near, _, _ = _check_index_rows(0, rows, g_idx, g_cnt, d["q_idx"][0], kbar_h[0], 2048)
-    say("cfg0 near-tie differences:", near)
-    for (_, i, blk, *_r) in d["plants"]:
+    say("4K fp32 near-tie differences:", near)
+    for (_, i, blk, *_r) in _intact_plants(d["plants"]):
         assert blk in set(g_idx[0, i, :g_cnt[0, i]].tolist())
     o = oracle.attend_rows(d["q"][0], d["k"][0], d["v"][0], rows, g_idx[0], g_cnt[0])
     err = rel_err(g_out[0], o)
-    say("cfg0 attention rel err", err)
+    say("4K fp32 attention rel err", err)
     assert err <= TOL["fp32"]
 
 
@@ -221,7 +231,7 @@ def test_bf16_medium_end_to_end_and_chunking():
         err = rel_err(g_out[b][rows], o)
         say("medium seq", b, "attention rel err", err)
         assert err <= TOL["bf16"]
-    for (b, i, blk, *_r) in d["plants"]:
+    for (b, i, blk, *_r) in _intact_plants(d["plants"]):
         assert blk in set(g_idx[b, i, :g_cnt[b, i]].tolist())
 
 
@@ -351,59 +361,100 @@ def test_decode_exact_route_on_ties():
 
 # ---- full-size configurations, sampled rows --------------------------------
 
-def _sample_rows(n, plants, seed=0, nrand=96):
+def _sample_rows(n, plants, nrand, seed=0):
+    """Rows 0-7, the dense -> sparse transition 2040-2061, nrand uniform rows,
+    the last 8 rows and the query row of every planted match."""
     rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([np.arange(8), np.arange(2040, 2062), rng.integers(0, n, nrand),
-                                     np.arange(n - 8, n), [pl[1] for pl in plants[:16]]]))
+    return np.unique(np.concatenate([np.arange(8), np.arange(2040, 2062),
+                                     rng.integers(0, n, nrand), np.arange(n - 8, n),
+                                     [pl[1] for pl in plants]])).astype(np.int64)
 
 
-# cfg4p (1M tokens, 8192 query tiles) runs the indexer in four groups of
-# tiles that reuse one workspace; cfg1 and cfg2 fit one group
-@pytest.mark.parametrize("cfg", ["cfg1", "cfg2", "cfg4p"])
-def test_full_size_prefill_sampled(cfg):
+def _sample_blocks(nb, seed=1):
+    """Pooled-key blocks checked at full size: the first and last 64, six
+    more runs of 64 spread over the sequence, 256 uniform singles."""
+    rng = np.random.default_rng(seed)
+    runs = [0, nb - 64] + [int(x) for x in rng.integers(0, nb - 64, 6)]
+    blocks = np.concatenate([np.arange(b0, b0 + 64) for b0 in runs] +
+                            [rng.integers(0, nb, 256)])
+    return np.unique(blocks).astype(np.int64)
+
+
+def _check_pool_sampled(tag, kbar_h, k_idx_h, nb):
+    """GPU pooled keys of sampled blocks (positions up to the sequence end)
+    within one bf16 ulp of the oracle's."""
+    blocks = _sample_blocks(nb)
+    # contiguous runs go to the oracle as ranges [b0, b1)
+    splits = np.nonzero(np.diff(blocks) != 1)[0] + 1
+    worst = 0.0
+    for run in np.split(blocks, splits):
+        b0, b1 = int(run[0]), int(run[-1]) + 1
+        ref = as_f64(oracle.pool(k_idx_h, b0=b0, b1=b1))
+        got = as_f64(kbar_h[b0:b1])
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+        ratio = np.abs(got - ref) / ulp
+        worst = max(worst, float(ratio.max()))
+        assert np.all(ratio <= 1.0), "%s: pooled keys of blocks [%d, %d) differ by %.2f ulp" % (
+            tag, b0, b1, ratio.max())
+    say(tag, "pooled keys: %d blocks up to block %d, max %.2f bf16 ulp" % (
+        blocks.size, int(blocks.max()), worst))
+
+
+def _check_index_at(tag, q_rows_h, kbar_h, pos, g_idx, g_cnt):
+    """Selections of rows given with their positions against the oracle, with
+    the near-tie rule; returns the oracle selection."""
+    o_idx, o_cnt = oracle.index_at(q_rows_h, kbar_h, pos)
+    assert np.array_equal(g_cnt, o_cnt), "%s: counts differ" % tag
+    differ = np.array([u for u in range(len(pos)) if not np.array_equal(g_idx[u], o_idx[u])],
+                      dtype=np.int64)
+    near = 0
+    if differ.size:
+        sc = oracle.score_at(q_rows_h[differ], kbar_h, pos[differ])
+        near = check_sets(g_idx[differ], g_cnt[differ], o_idx[differ], o_cnt[differ], sc)
+    say(tag, "%d rows, %d differ, %d near-tie blocks" % (len(pos), differ.size, near))
+    return o_idx, o_cnt
+
+
+# the 1M-token prefill (8192 query tiles) runs the indexer in four groups of
+# tiles that reuse one workspace; 64K and 256K fit one group
+@pytest.mark.parametrize("cfg,nrand", [("prefill_64k", 1024), ("prefill_256k", 1024),
+                                       ("prefill_1m", 256)])
+def test_full_size_prefill_sampled(cfg, nrand):
     say("full-size prefill", cfg)
-    d = inputs.make(cfg, seed={"cfg1": 101, "cfg2": 102, "cfg4p": 104}[cfg], backend="torch")
+    d = inputs.make(cfg, seed={"prefill_64k": 101, "prefill_256k": 102, "prefill_1m": 104}[cfg],
+                    backend="torch")
     p = _params()
     n = d["n"]
     kbar, idx, cnt, out = qsa.prefill(p, d["k_idx"], d["q_idx"], d["q"], d["k"], d["v"])
     torch.cuda.synchronize()
-    rows = _sample_rows(n, d["plants"])
-    rt = torch.from_numpy(rows).cuda()
     kbar_h = to_host(kbar[0])
+    _check_pool_sampled(cfg, kbar_h, to_host(d["k_idx"][0]), n // 4)
+    rows = _sample_rows(n, d["plants"], nrand)
+    rt = torch.from_numpy(rows).cuda()
     qi_h = to_host(d["q_idx"][0][rt])
     g_idx, g_cnt = to_host(idx[0][rt]), to_host(cnt[0][rt])
-    # oracle on the sampled rows: rows are re-indexed 0..len-1, positions kept
-    o_idx = np.empty_like(g_idx)
-    o_cnt = np.empty_like(g_cnt)
-    sc = []
-    for u, i in enumerate(rows):
-        oi, oc = oracle.index_rows(qi_h[u:u + 1], kbar_h, [0], int(i))
-        o_idx[u], o_cnt[u] = oi[0], oc[0]
-        sc.append(oracle.score_rows(qi_h[u:u + 1], kbar_h, [0], int(i))[0])
-    near = check_sets(g_idx, g_cnt, o_idx, o_cnt, sc)
-    say(cfg, "near-tie differences", near)
-    for (_, i, blk, *_r) in d["plants"][:16]:
-        u = int(np.nonzero(rows == i)[0][0])
-        assert blk in set(g_idx[u, :g_cnt[u]].tolist())
+    _check_index_at(cfg, qi_h, kbar_h, rows, g_idx, g_cnt)
+    intact = _intact_plants(d["plants"])
+    say(cfg, "%d of %d planted matches intact" % (len(intact), len(d["plants"])))
+    for (_, i, blk, *_r) in intact:
+        u = int(np.searchsorted(rows, i))
+        assert blk in set(g_idx[u, :g_cnt[u]].tolist()), "planted block %d of row %d" % (blk, i)
     k_h, v_h = to_host(d["k"][0]), to_host(d["v"][0])
-    q_h = to_host(d["q"][0][rt])
-    errs = []
-    for u, i in enumerate(rows):
-        o = oracle.attend_rows(q_h[u:u + 1], k_h, v_h, [0], g_idx[u:u + 1], g_cnt[u:u + 1],
-                               pos0=int(i))
-        errs.append((as_f64(to_host(out[0][int(i)])), o[0]))
-    err = rel_err(np.stack([e[0] for e in errs]), np.stack([e[1] for e in errs]))
-    say(cfg, "attention rel err", err)
+    o = oracle.attend_at(to_host(d["q"][0][rt]), k_h, v_h, rows, g_idx, g_cnt)
+    err = rel_err(to_host(out[0][rt]), o)
+    say(cfg, "attention rel err over %d rows" % rows.size, err)
     assert err <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("cfg,check", [("cfg3", [0, 63]), ("cfg4d", [0, 7])])
-def test_full_size_decode_sampled(cfg, check):
+@pytest.mark.parametrize("cfg", ["decode_64x256k", "decode_8x1m"])
+def test_full_size_decode_sampled(cfg):
     say("full-size decode", cfg)
-    d = inputs.make(cfg, seed=100 + int(cfg[3]), backend="torch")
+    d = inputs.make(cfg, seed={"decode_64x256k": 103, "decode_8x1m": 104}[cfg], backend="torch")
     p = _params()
     B, L = d["B"], d["n"]
     nb = L // 4
+    # 64 x 256K: 17 of the 64 sequences (every fourth, and the last); 8 x 1M: all 8
+    check = list(range(0, B, 4)) + [B - 1] if B > 8 else list(range(B))
     kbar = _pool_gpu(p, d["k_idx"], nb)
     seq_len = torch.full((B,), L, dtype=torch.int32, device="cuda")
     idx, cnt = _index_gpu(p, d["q_idx"], kbar, seq_len=seq_len)
@@ -413,18 +464,19 @@ def test_full_size_decode_sampled(cfg, check):
     torch.cuda.synchronize()
     for b in check:
         kbar_h = to_host(kbar[b])
+        if b in (check[0], check[-1]):
+            _check_pool_sampled("%s seq %d" % (cfg, b), kbar_h, to_host(d["k_idx"][b]), nb)
         qi = to_host(d["q_idx"][b, 0])
-        o_idx, o_cnt = oracle.index_rows(qi[None], kbar_h, [0], L - 1)
-        sc = oracle.score_rows(qi[None], kbar_h, [0], L - 1)
         g_idx, g_cnt = to_host(idx[b]), to_host(cnt[b])
-        check_sets(g_idx, g_cnt, o_idx, o_cnt, sc)
+        _check_index_at("%s seq %d" % (cfg, b), qi[None], kbar_h, np.array([L - 1]), g_idx,
+                        g_cnt)
         # planted blocks outscore every noise block; when a sequence has more
         # planted blocks than k_B, the selection holds k_B of them
         planted = {blk for (bb, i, blk, *_r) in d["plants"] if bb == b}
         sel = set(g_idx[0, :g_cnt[0]].tolist())
         assert len(sel & planted) == min(len(planted), int(g_cnt[0]))
-        o = oracle.attend_rows(to_host(d["q"][b]), to_host(d["k"][b]), to_host(d["v"][b]), [0],
-                               g_idx, g_cnt, pos0=L - 1)
+        o = oracle.attend_at(to_host(d["q"][b]), to_host(d["k"][b]), to_host(d["v"][b]),
+                             np.array([L - 1]), g_idx, g_cnt)
         err = rel_err(to_host(out[b]), o)
         say(cfg, "seq", b, "attention rel err", err)
         assert err <= TOL["bf16"]

@@ -214,7 +214,7 @@ def test_toy_selection_and_token_sets():
 
 
 def test_planted_blocks_are_selected():
-    d = inputs.make("cfg0", seed=100)
+    d = inputs.make("prefill_4k_fp32", seed=100)
     kbar = oracle.pool(d["k_idx"][0])
     rows = sorted({p[1] for p in d["plants"]})
     idx, cnt = oracle.index_rows(d["q_idx"][0], kbar, rows)
@@ -310,6 +310,26 @@ def test_decode_equals_last_prefill_row():
                                d["v"][0], seq_len=n)
     assert dc == cnt[0] and np.array_equal(di, idx[0])
     np.testing.assert_array_equal(do, out[0])
+
+
+def test_rows_given_by_position_equal_prefill_rows():
+    """index_at / score_at / attend_at take a compacted set of rows with
+    their positions (sampled parity of long sequences); they must address
+    the same rows as the prefill-row functions."""
+    n = 3000
+    d = inputs.small(n=n, hq=8, hkv=2, dtype="bf16", seed=14, planted=4)
+    kbar = oracle.pool(d["k_idx"][0])
+    rows = np.array([0, 5, 2050, 2051, 2999, 1234])
+    idx, cnt = oracle.index_rows(d["q_idx"][0], kbar, rows, K=512)
+    ia, ca = oracle.index_at(d["q_idx"][0][rows], kbar, rows, K=512)
+    assert np.array_equal(idx, ia) and np.array_equal(cnt, ca)
+    sc = oracle.score_rows(d["q_idx"][0], kbar, rows)
+    sa = oracle.score_at(d["q_idx"][0][rows], kbar, rows)
+    for x, y in zip(sc, sa):
+        assert np.array_equal(x, y)
+    out = oracle.attend_rows(d["q"][0], d["k"][0], d["v"][0], rows, idx, cnt)
+    oa = oracle.attend_at(d["q"][0][rows], d["k"][0], d["v"][0], rows, ia, ca)
+    assert np.array_equal(out, oa)
 
 
 def test_generator_is_deterministic():

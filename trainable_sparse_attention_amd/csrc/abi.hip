@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include "qsa_internal.h"
+#include "../../include/qsa_probe.h"
 
 using namespace qsa;
 
@@ -135,7 +136,15 @@ qsa_status qsa_index_topk(const qsa_params* p, qsa_dtype dtype, const void* q_id
   const int kB = qsa_k_blocks(p);
   if (B == 0) return QSA_OK;
   const bool dec = d_seq_len && decode_split_path(n_q);
-  if (dec && kB > 4096) return fail(QSA_ERR_UNSUPPORTED, "decode path built for k_B <= 4096");
+  // the candidate lists of the many-row kernels hold 4096 entries and are cut
+  // back to k_B whenever a stage could overflow them: k_B must stay well
+  // below that; the decode lists hold 6016
+  if (!dec && kB > kMaxKBlocksRows)
+    return fail(QSA_ERR_UNSUPPORTED, "k_B=%d: the many-row indexer is built for k_B <= %d", kB,
+                kMaxKBlocksRows);
+  if (dec && kB > kMaxKBlocksDecode)
+    return fail(QSA_ERR_UNSUPPORTED, "k_B=%d: the decode indexer is built for k_B <= %d", kB,
+                kMaxKBlocksDecode);
   const size_t need = qsa_index_topk_workspace(p, dtype, B, n_q, nb_cap, d_seq_len != nullptr);
   if (!workspace || workspace_bytes < need)
     return fail(QSA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
@@ -171,6 +180,10 @@ static qsa_status check_attn(const qsa_params* p, qsa_dtype dtype, const void* q
   if (hq % hkv) return fail(QSA_ERR_SHAPE, "hq=%d not a multiple of hkv=%d", hq, hkv);
   if (hq / hkv > 16) return fail(QSA_ERR_UNSUPPORTED, "hq/hkv=%d > 16", hq / hkv);
   if (d != 128) return fail(QSA_ERR_UNSUPPORTED, "head dim %d: only 128", d);
+  // the bf16 kernels address a head's K/V rows with 32-bit byte offsets
+  if (dtype == QSA_BF16 && n_cap > kMaxCapBf16)
+    return fail(QSA_ERR_UNSUPPORTED, "n_cap=%lld: bf16 attention is built for n_cap <= %lld",
+                (long long)n_cap, (long long)kMaxCapBf16);
   return QSA_OK;
 }
 
@@ -246,6 +259,40 @@ qsa_status qsa_sparse_attn_decode(const qsa_params* p, qsa_dtype dtype, const vo
   a.scale = scale > 0.f ? scale : 1.f / sqrtf((float)d);
   return launched(launch_attn_decode(dtype, a, workspace, (hipStream_t)stream),
                   "sparse_attn_decode");
+}
+
+qsa_status qsa_probe_gather(const qsa_params* p, const void* k, const void* v, int64_t n_cap,
+                            const int32_t* idx, const int32_t* cnt, int32_t B, int32_t n_q,
+                            int64_t q_pos0, int32_t hkv, int32_t waves_per_cu, int32_t depth,
+                            uint32_t* sink, void* stream) {
+  qsa_status s = check_attn(p, QSA_BF16, k, k, v, idx, cnt, sink, B, n_q, hkv, hkv, 128, n_cap);
+  if (s) return s;
+  if (p->r != 4) return fail(QSA_ERR_UNSUPPORTED, "the probe reads 4-token blocks");
+  if (qsa_k_blocks(p) % 8) return fail(QSA_ERR_UNSUPPORTED, "the probe needs k_B % 8 == 0");
+  if (depth < 1 || depth > 4) return fail(QSA_ERR_SHAPE, "depth=%d outside 1..4", depth);
+  if (q_pos0 < 0 || q_pos0 + n_q > n_cap)
+    return fail(QSA_ERR_SHAPE, "positions [%lld, %lld) exceed n_cap=%lld", (long long)q_pos0,
+                (long long)(q_pos0 + n_q), (long long)n_cap);
+  if (B == 0) return QSA_OK;
+  AttnArgs a;
+  a.q = nullptr;
+  a.k = k;
+  a.v = v;
+  a.out = nullptr;
+  a.idx = idx;
+  a.cnt = cnt;
+  a.seq_len = nullptr;
+  a.n_cap = n_cap;
+  a.q_pos0 = q_pos0;
+  a.B = B;
+  a.n_q = n_q;
+  a.hq = hkv;
+  a.hkv = hkv;
+  a.kB = qsa_k_blocks(p);
+  a.r = p->r;
+  a.scale = 1.f;
+  return launched(launch_probe_gather(a, waves_per_cu, depth, sink, (hipStream_t)stream),
+                  "probe_gather");
 }
 
 }  // extern "C"

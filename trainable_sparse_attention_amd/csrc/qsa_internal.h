@@ -57,6 +57,16 @@ __device__ __forceinline__ void rope_cs(int64_t pos, int j, int R, double log2_t
   *s = (float)sn;
 }
 
+// ---- limits the host checks before any launch ----------------------------
+// Largest k_B of the many-row indexer (candidate lists of 4096 entries, cut
+// back to k_B whenever one more LDS stage of blocks could overflow them).
+constexpr int kMaxKBlocksRows = 3072;
+// Largest k_B of the few-token decode indexer (candidate lists of 6016).
+constexpr int kMaxKBlocksDecode = 4096;
+// Largest KV capacity of the bf16 attention: a token row's byte offset
+// within one head, row * 256, is formed in 32 bits.
+constexpr int64_t kMaxCapBf16 = (int64_t)1 << 24;
+
 // ---- host launchers (defined in the kernel translation units) ------------
 
 hipError_t launch_pool(qsa_dtype dt, const qsa_params& p, const void* k_idx, int64_t n_cap,
@@ -104,5 +114,7 @@ struct AttnArgs {
 hipError_t launch_attn_prefill(qsa_dtype dt, const AttnArgs& a, hipStream_t st);
 size_t attn_decode_workspace(int B, int n_q, int hkv, int kB);
 hipError_t launch_attn_decode(qsa_dtype dt, const AttnArgs& a, void* ws, hipStream_t st);
+hipError_t launch_probe_gather(const AttnArgs& a, int waves_per_cu, int depth, uint32_t* sink,
+                               hipStream_t st);
 
 }  // namespace qsa

@@ -17,8 +17,9 @@ the indexer dims that are not position-rotated (64..127), k_idx = c *
 q_idx[i, h] for a random indexer head h, and zeros on the rotated dims
 (0..63), so the match does not depend on the distance between i and b; in
 the attention KV head g of a random query head a, k[g, token] = 4 c *
-q[i, a].  c is drawn uniform in [2, 4] (config 0 uses c = 4 exactly).
-Decode configurations plant against the one new query of each sequence.
+q[i, a].  c is drawn uniform in [2, 4] (the 4K-token float32 workload uses
+c = 4 exactly).  Decode workloads plant against the last new query of each
+sequence.
 
 Two generators exist: ``numpy`` (Philox on the host; used by the CPU tests
 and the small GPU parity cases) and ``torch`` (Philox on the GPU through
@@ -32,17 +33,37 @@ import numpy as np
 
 R, K_TOP, H_IDX, D_IDX, ROPE_DIMS, THETA, D_HEAD = 4, 2048, 4, 128, 64, 10000.0, 128
 
-# The five workloads: prefill rows are positions 0..n-1 of each sequence;
-# a decode sequence holds seq_len tokens, the last of which is the query.
+# The workloads: prefill rows are positions 0..n-1 of each sequence; a decode
+# sequence holds n tokens, the last n_new of which are the new queries (the
+# pages' decode benchmark takes 4 new tokens per step: 1 + 3 drafts).
 CONFIGS = {
-    "cfg0": dict(mode="prefill", B=1, n=4096, hq=4, hkv=1, dtype="fp32", planted=16,
-                 plant_c=4.0),
-    "cfg1": dict(mode="prefill", B=1, n=65536, hq=16, hkv=2, dtype="bf16", planted=256),
-    "cfg2": dict(mode="prefill", B=1, n=262144, hq=16, hkv=2, dtype="bf16", planted=256),
-    "cfg3": dict(mode="decode", B=64, n=262144, hq=16, hkv=2, dtype="bf16", planted=64),
-    "cfg4p": dict(mode="prefill", B=1, n=1048576, hq=16, hkv=2, dtype="bf16", planted=1024),
-    "cfg4d": dict(mode="decode", B=8, n=1048576, hq=16, hkv=2, dtype="bf16", planted=1024),
+    "prefill_4k_fp32": dict(mode="prefill", B=1, n=4096, hq=4, hkv=1, dtype="fp32",
+                            planted=16, plant_c=4.0),
+    "prefill_64k": dict(mode="prefill", B=1, n=65536, hq=16, hkv=2, dtype="bf16", planted=256),
+    "prefill_256k": dict(mode="prefill", B=1, n=262144, hq=16, hkv=2, dtype="bf16",
+                         planted=256),
+    "decode_64x256k": dict(mode="decode", B=64, n=262144, hq=16, hkv=2, dtype="bf16",
+                           planted=64),
+    "prefill_1m": dict(mode="prefill", B=1, n=1048576, hq=16, hkv=2, dtype="bf16",
+                       planted=1024),
+    "decode_8x1m": dict(mode="decode", B=8, n=1048576, hq=16, hkv=2, dtype="bf16",
+                        planted=1024),
+    "decode_4x1m_next4": dict(mode="decode", B=4, n=1048576, n_new=4, hq=16, hkv=2,
+                              dtype="bf16", planted=1024),
 }
+
+
+def describe(name):
+    """The workload's sizes in words."""
+    c = CONFIGS[name]
+    dt = "bf16" if c["dtype"] == "bf16" else "float32"
+    heads = "indexer 4x128 query heads + 1x128 key head, attention %d q / %d kv heads, d=128" % (
+        c["hq"], c["hkv"])
+    if c["mode"] == "prefill":
+        return "QSA prefill, batch %d, n=%d tokens, K=2048, r=4, %s, %s" % (c["B"], c["n"],
+                                                                         heads, dt)
+    return "QSA decode, batch %d, %d cached tokens per sequence, %d new token(s), K=2048, " \
+           "r=4, %s, %s" % (c["B"], c["n"], c.get("n_new", 1), heads, dt)
 
 
 def k_blocks(K=K_TOP, r=R):
@@ -73,12 +94,13 @@ def _plant_rows(rng, mode, n, planted, kB, r):
     return rows, blocks
 
 
-def make(cfg="cfg0", seed=0, backend="numpy", device="cuda", overrides=None):
+def make(cfg="prefill_4k_fp32", seed=0, backend="numpy", device="cuda", overrides=None):
     """Inputs of one configuration.
 
     Returns a dict with the shapes and
       q_idx [B][n_q][4][128], k_idx [B][n][128], q [B][n_q][hq][128],
-      k, v [B][hkv][n][128]  (n_q = n for prefill, 1 for decode),
+      k, v [B][hkv][n][128]  (n_q = n for prefill, n_new (default 1) for
+      decode: the queries of positions n - n_q .. n - 1),
       plants: list of (seq, row, block, idx_head, attn_head, c).
     numpy backend: float32 arrays or bf16 bit patterns (uint16).
     torch backend: torch tensors on `device` (float32 or bfloat16)."""
@@ -90,7 +112,7 @@ def make(cfg="cfg0", seed=0, backend="numpy", device="cuda", overrides=None):
     plant_c = spec.get("plant_c", None)
     r = spec.get("r", R)
     kB = k_blocks(spec.get("K", K_TOP), r)
-    n_q = n if mode == "prefill" else 1
+    n_q = n if mode == "prefill" else spec.get("n_new", 1)
     bf16 = spec["dtype"] == "bf16"
     inv = 1.0 / math.sqrt(128.0)
     shapes = dict(q_idx=(B, n_q, H_IDX, D_IDX), k_idx=(B, n, D_IDX), q=(B, n_q, hq, D_HEAD),
@@ -113,7 +135,7 @@ def make(cfg="cfg0", seed=0, backend="numpy", device="cuda", overrides=None):
             for t in range(planted):
                 i, blk, h, a, c = int(rows[t]), int(blocks[t]), int(heads[t]), int(aheads[t]), \
                     float(cs[t])
-                qi = 0 if mode == "decode" else i
+                qi = n_q - 1 if mode == "decode" else i
                 g = (a * hkv) // hq
                 for tok in range(blk * r, blk * r + r):
                     arrs["k_idx"][b, tok, :ROPE_DIMS] = 0.0
@@ -155,7 +177,7 @@ def make(cfg="cfg0", seed=0, backend="numpy", device="cuda", overrides=None):
             for t in range(planted):
                 i, blk, h, a, c = int(rows[t]), int(blocks[t]), int(heads[t]), int(aheads[t]), \
                     float(cs[t])
-                qi = 0 if mode == "decode" else i
+                qi = n_q - 1 if mode == "decode" else i
                 gk = (a * hkv) // hq
                 src_i = res["q_idx"][b, qi, h, :].float() * c
                 src_i[:ROPE_DIMS] = 0.0

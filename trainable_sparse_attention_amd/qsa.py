@@ -16,11 +16,11 @@ QSA_FP32, QSA_BF16 = 0, 1
 STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL", 2: "QSA_ERR_SHAPE", 3: "QSA_ERR_DTYPE",
           4: "QSA_ERR_UNSUPPORTED", 5: "QSA_ERR_WORKSPACE", 6: "QSA_ERR_LAUNCH"}
 
-# every symbol include/qsa.h declares
+# every symbol the headers in include/ declare
 EXPORTS = ["qsa_default_params", "qsa_k_blocks", "qsa_status_str", "qsa_last_error",
            "qsa_pool_keys", "qsa_index_topk", "qsa_index_topk_workspace",
            "qsa_sparse_attn_prefill", "qsa_sparse_attn_decode",
-           "qsa_sparse_attn_decode_workspace"]
+           "qsa_sparse_attn_decode_workspace", "qsa_probe_gather"]
 
 
 class QSAError(RuntimeError):
@@ -72,6 +72,8 @@ def lib():
         L.qsa_sparse_attn_decode.restype = ctypes.c_int
         L.qsa_sparse_attn_decode_workspace.argtypes = [PP, I32, I32, I32, I32, I32]
         L.qsa_sparse_attn_decode_workspace.restype = SZ
+        L.qsa_probe_gather.argtypes = [PP, P, P, I64, P, P, I32, I32, I64, I32, I32, I32, P, P]
+        L.qsa_probe_gather.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -156,6 +158,16 @@ def qsa_sparse_attn_decode(p, q, k_cache, v_cache, seq_len, idx, cnt, out, works
                                         B, n_q, hq, hkv, d, scale, _ptr(out), _ptr(workspace),
                                         0 if workspace is None else workspace.numel(),
                                         _stream(stream)))
+
+
+def qsa_probe_gather(p, k, v, idx, cnt, sink, waves_per_cu=8, depth=1, q_pos0=0, stream=None):
+    """Memory-only replay of the prefill attention's gathers (measurement
+    aid; include/qsa_probe.h).  sink: uint32 [B * n_q * hkv]."""
+    B, hkv, n_cap = k.shape[0], k.shape[1], k.shape[2]
+    n_q = idx.shape[1]
+    _check(lib().qsa_probe_gather(ctypes.byref(p), _ptr(k), _ptr(v), n_cap, _ptr(idx), _ptr(cnt),
+                                  B, n_q, q_pos0, hkv, waves_per_cu, depth, _ptr(sink),
+                                  _stream(stream)))
 
 
 # ---- the whole path (sequences of the calls above) -------------------------
