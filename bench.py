@@ -13,9 +13,9 @@ setting) under "decode_more".
 
 Timing: HIP events recorded on the stream the kernels run on (torch's current
 stream) around every step and stage.  Before each timed step an untimed
-512 MB fill evicts L2 and the memory-side cache, so every step starts cold;
-the same steps back to back without it are reported under "unflushed".  GPU
-clocks are read before and after the timed region.
+512 MB read evicts L2 and the memory-side cache, so every step starts cold;
+the same steps back to back without it are reported under "unflushed".  The
+graphics clock is sampled on a host thread during the timed steps.
 
 The roofline object describes the kernel that takes the most time (the
 prefill attention) against the bf16 MFMA peak with its algorithmic FLOPs; its
@@ -68,21 +68,53 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def gpu_clocks():
-    """Current graphics and memory clocks of device 0 (MHz), best effort."""
-    try:
-        import amdsmi
-        amdsmi.amdsmi_init()
+class ClockSampler:
+    """Samples the graphics clock of device 0 (amdsmi) every few ms on a
+    host thread while the timed steps run; reports min / median / max MHz.
+    Informative only: any failure is recorded, not raised."""
+
+    def __init__(self):
+        self.vals, self.err, self._stop = [], None, None
         try:
-            h = amdsmi.amdsmi_get_processor_handles()[0]
-            gfx = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
-            mem = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.MEM)
-            return {"gfx_mhz": gfx.get("clk"), "gfx_max_mhz": gfx.get("max_clk"),
-                    "mem_mhz": mem.get("clk")}
-        finally:
-            amdsmi.amdsmi_shut_down()
-    except Exception as e:  # the reading is informative only
-        return {"error": str(e)[:120]}
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception as e:
+            self._smi, self.err = None, str(e)[:120]
+
+    def __enter__(self):
+        import threading
+        self.vals = []
+        if self._smi is None:
+            return self
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                try:
+                    c = self._smi.amdsmi_get_clock_info(self._h, self._smi.AmdSmiClkType.GFX)
+                    self.vals.append(c.get("clk"))
+                except Exception as e:
+                    self.err = str(e)[:120]
+                    return
+                self._stop.wait(0.005)
+
+        self._t = threading.Thread(target=run, daemon=True)
+        self._t.start()
+        return self
+
+    def __exit__(self, *a):
+        if self._stop is not None:
+            self._stop.set()
+            self._t.join()
+
+    def summary(self):
+        v = sorted(x for x in self.vals if isinstance(x, (int, float)))
+        if not v:
+            return {"error": self.err or "no samples"}
+        return {"gfx_mhz_min": v[0], "gfx_mhz_median": v[len(v) // 2], "gfx_mhz_max": v[-1],
+                "samples": len(v)}
 
 
 def recorded_traffic(kernel):
@@ -116,17 +148,18 @@ def sum_nb(n, r=4):
 
 
 class Flusher:
-    """An untimed 512 MB fill between timed steps: L2 (4 MB per XCD) and the
-    256 MB memory-side cache then hold none of the step's inputs."""
+    """An untimed read of a 512 MB buffer between timed steps: L2 (4 MB per
+    XCD) and the 256 MB memory-side cache then hold none of the step's
+    inputs, and the previous step's dirty outputs have been written back (a
+    read leaves clean lines, so the timed step pays for no write-back)."""
 
     def __init__(self, torch, enabled):
-        self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda") if enabled else None
-        self.k = 0
+        self.buf = torch.ones(FLUSH_BYTES // 8, dtype=torch.int64, device="cuda") \
+            if enabled else None
 
     def __call__(self):
         if self.buf is not None:
-            self.k = (self.k + 1) & 0xFF
-            self.buf.fill_(self.k)
+            self.acc = self.buf.sum()
 
 
 def time_steps(torch, stream, stages, K, flush):
@@ -173,11 +206,11 @@ def bench_prefill(args, torch, qsa, inputs, flush):
         for f in stages:
             f()
     torch.cuda.synchronize()
-    clk0 = gpu_clocks()
+    clocks = ClockSampler()
     t0 = time.perf_counter()
-    ms, st = time_steps(torch, stream, stages, args.steps, flush)
+    with clocks:
+        ms, st = time_steps(torch, stream, stages, args.steps, flush)
     wall = time.perf_counter() - t0
-    clk1 = gpu_clocks()
     ms_u, st_u = time_steps(torch, stream, stages, args.steps, lambda: None)
     # algorithmic work
     pairs = sum_nb(n, p.r) * B
@@ -194,7 +227,7 @@ def bench_prefill(args, torch, qsa, inputs, flush):
     res = dict(n=n, B=B, ms=ms, wall_ms=wall * 1000 / args.steps, stage_ms=st, pairs=pairs,
                slots=slots, idx_flop=idx_flop, attn_flop=attn_flop, attn_bytes=attn_bytes,
                gather_bytes=gather_bytes, pool_bytes=pool_bytes, tok_s=B * n / (ms * 1e-3),
-               ms_unflushed=ms_u, stage_ms_unflushed=st_u, clocks=[clk0, clk1])
+               ms_unflushed=ms_u, stage_ms_unflushed=st_u, clocks=clocks.summary())
     probe = None
     if not args.no_probe:
         probe = probe_sweep(torch, qsa, p, d, idx, cnt, flush, stream)
@@ -211,7 +244,8 @@ def probe_sweep(torch, qsa, p, d, idx, cnt, flush, stream):
         best = None
         for _ in range(2):
             ms, _ = time_steps(torch, stream, [lambda: qsa.qsa_probe_gather(
-                p, d["k"], d["v"], idx, cnt, sink, w, depth, 0, stream)], 1, flush)
+                p, d["k"], d["v"], idx, cnt, sink, waves_per_cu=w, depth=depth,
+                stream=stream)], 1, flush)
             best = ms if best is None else min(best, ms)
         pts.append({"waves_per_cu": w, "depth": depth, "ms": best})
         log("gather probe: %s waves/CU, depth %d: %.3f ms" % (w or "max", depth, best))
@@ -287,7 +321,7 @@ def decode_record(inputs, dec, steps):
         "value": dec["tok_s"], "unit": "tokens/s", "ms_per_step": dec["ms"],
         "steps": steps, "workload": inputs.describe(dec["name"]),
         "timing": "one HIP graph replay per step (the three calls captured once), "
-                  "512 MB cache flush before each step",
+                  "untimed 512 MB read before each step",
         "ms_per_step_unflushed": dec["ms_unflushed"],
         "eager_ms_per_step": dec["eager_ms"],
         "eager_stage_ms": {"pool_keys": dec["stage_ms"][0], "index_topk": dec["stage_ms"][1],
@@ -413,13 +447,14 @@ def main():
                    "seq_len": pre["n"], "parallelism": "none"},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "timing": "HIP events per step on the kernels' stream; 512 MB cache flush before each "
-                  "timed step (not timed)" if not args.no_flush else "HIP events, back to back",
+        "timing": "HIP events per step on the kernels' stream; an untimed 512 MB read before "
+                  "each timed step evicts the caches" if not args.no_flush else
+                  "HIP events, back to back",
         "unflushed": {"ms_per_step": pre["ms_unflushed"],
                       "tokens/s": pre["B"] * pre["n"] / (pre["ms_unflushed"] * 1e-3),
                       "stage_ms": dict(zip(["pool_keys", "index_topk", "sparse_attn_prefill"],
                                            pre["stage_ms_unflushed"]))},
-        "clocks": {"before": pre["clocks"][0], "after": pre["clocks"][1]},
+        "clocks": pre["clocks"],
         "stages": {
             "pool_keys": {"ms": st[0], "GB/s": pre["pool_bytes"] / (st[0] * 1e-3) / 1e9,
                           "frac_hbm": pre["pool_bytes"] / (st[0] * 1e-3) / 1e9 / PEAK_HBM_GBS},

@@ -15,10 +15,14 @@
  *   waves_per_cu : the per-wave LDS request is the CU's LDS / waves_per_cu
  *                  (<= 0: no extra request, occupancy set by registers)
  *   depth    : chunks of 8 slots kept in flight per wave, 1..4
- *   sink     : device uint32 [B * n_q * hkv], one word written per wave
+ *   rows_per_wave : 1..64 consecutive query rows per wave, swept in lock
+ *                  step (each step reads one chunk of every row); 1 is the
+ *                  attention kernel's own mapping
+ *   sink     : device uint32 [B * ceil(n_q / rows_per_wave) * hkv], one word
+ *              written per wave
  * Errors: NULL pointers, sizes as for qsa_sparse_attn_prefill, r != 4,
- * k_B not a multiple of 8, depth outside 1..4 -> non-zero status (see
- * qsa.h), nothing launched.
+ * k_B not a multiple of 8, depth or rows_per_wave out of range -> non-zero
+ * status (see qsa.h), nothing launched.
  */
 #ifndef QSA_PROBE_H
 #define QSA_PROBE_H
@@ -32,7 +36,7 @@ extern "C" {
 qsa_status qsa_probe_gather(const qsa_params* p, const void* k, const void* v, int64_t n_cap,
                             const int32_t* idx, const int32_t* cnt, int32_t B, int32_t n_q,
                             int64_t q_pos0, int32_t hkv, int32_t waves_per_cu, int32_t depth,
-                            uint32_t* sink, void* stream);
+                            int32_t rows_per_wave, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -264,12 +264,14 @@ qsa_status qsa_sparse_attn_decode(const qsa_params* p, qsa_dtype dtype, const vo
 qsa_status qsa_probe_gather(const qsa_params* p, const void* k, const void* v, int64_t n_cap,
                             const int32_t* idx, const int32_t* cnt, int32_t B, int32_t n_q,
                             int64_t q_pos0, int32_t hkv, int32_t waves_per_cu, int32_t depth,
-                            uint32_t* sink, void* stream) {
+                            int32_t rows_per_wave, uint32_t* sink, void* stream) {
   qsa_status s = check_attn(p, QSA_BF16, k, k, v, idx, cnt, sink, B, n_q, hkv, hkv, 128, n_cap);
   if (s) return s;
   if (p->r != 4) return fail(QSA_ERR_UNSUPPORTED, "the probe reads 4-token blocks");
   if (qsa_k_blocks(p) % 8) return fail(QSA_ERR_UNSUPPORTED, "the probe needs k_B % 8 == 0");
   if (depth < 1 || depth > 4) return fail(QSA_ERR_SHAPE, "depth=%d outside 1..4", depth);
+  if (rows_per_wave < 1 || rows_per_wave > 64)
+    return fail(QSA_ERR_SHAPE, "rows_per_wave=%d outside 1..64", rows_per_wave);
   if (q_pos0 < 0 || q_pos0 + n_q > n_cap)
     return fail(QSA_ERR_SHAPE, "positions [%lld, %lld) exceed n_cap=%lld", (long long)q_pos0,
                 (long long)(q_pos0 + n_q), (long long)n_cap);
@@ -291,7 +293,8 @@ qsa_status qsa_probe_gather(const qsa_params* p, const void* k, const void* v, i
   a.kB = qsa_k_blocks(p);
   a.r = p->r;
   a.scale = 1.f;
-  return launched(launch_probe_gather(a, waves_per_cu, depth, sink, (hipStream_t)stream),
+  return launched(launch_probe_gather(a, waves_per_cu, depth, rows_per_wave, sink,
+                                      (hipStream_t)stream),
                   "probe_gather");
 }
 

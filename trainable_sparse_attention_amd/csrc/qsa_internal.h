@@ -114,7 +114,7 @@ struct AttnArgs {
 hipError_t launch_attn_prefill(qsa_dtype dt, const AttnArgs& a, hipStream_t st);
 size_t attn_decode_workspace(int B, int n_q, int hkv, int kB);
 hipError_t launch_attn_decode(qsa_dtype dt, const AttnArgs& a, void* ws, hipStream_t st);
-hipError_t launch_probe_gather(const AttnArgs& a, int waves_per_cu, int depth, uint32_t* sink,
-                               hipStream_t st);
+hipError_t launch_probe_gather(const AttnArgs& a, int waves_per_cu, int depth, int rg,
+                               uint32_t* sink, hipStream_t st);
 
 }  // namespace qsa

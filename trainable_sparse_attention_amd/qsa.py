@@ -72,7 +72,8 @@ def lib():
         L.qsa_sparse_attn_decode.restype = ctypes.c_int
         L.qsa_sparse_attn_decode_workspace.argtypes = [PP, I32, I32, I32, I32, I32]
         L.qsa_sparse_attn_decode_workspace.restype = SZ
-        L.qsa_probe_gather.argtypes = [PP, P, P, I64, P, P, I32, I32, I64, I32, I32, I32, P, P]
+        L.qsa_probe_gather.argtypes = [PP, P, P, I64, P, P, I32, I32, I64, I32, I32, I32, I32, P,
+                                       P]
         L.qsa_probe_gather.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -160,14 +161,15 @@ def qsa_sparse_attn_decode(p, q, k_cache, v_cache, seq_len, idx, cnt, out, works
                                         _stream(stream)))
 
 
-def qsa_probe_gather(p, k, v, idx, cnt, sink, waves_per_cu=8, depth=1, q_pos0=0, stream=None):
+def qsa_probe_gather(p, k, v, idx, cnt, sink, waves_per_cu=8, depth=1, rows_per_wave=1,
+                     q_pos0=0, stream=None):
     """Memory-only replay of the prefill attention's gathers (measurement
-    aid; include/qsa_probe.h).  sink: uint32 [B * n_q * hkv]."""
+    aid; include/qsa_probe.h).  sink: uint32, one word per wave."""
     B, hkv, n_cap = k.shape[0], k.shape[1], k.shape[2]
     n_q = idx.shape[1]
     _check(lib().qsa_probe_gather(ctypes.byref(p), _ptr(k), _ptr(v), n_cap, _ptr(idx), _ptr(cnt),
-                                  B, n_q, q_pos0, hkv, waves_per_cu, depth, _ptr(sink),
-                                  _stream(stream)))
+                                  B, n_q, q_pos0, hkv, waves_per_cu, depth, rows_per_wave,
+                                  _ptr(sink), _stream(stream)))
 
 
 # ---- the whole path (sequences of the calls above) -------------------------
