@@ -186,6 +186,29 @@ qsa_status qsa_sparse_attn_decode(const qsa_params* p, qsa_dtype dtype, const vo
 size_t qsa_sparse_attn_decode_workspace(const qsa_params* p, int32_t B, int32_t n_q, int32_t hq,
                                         int32_t hkv, int32_t d);
 
+/*
+ * qsa_sparse_attn_decode_noalloc -- qsa_sparse_attn_decode for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same kernels and results,
+ * with the split partials kept in a fixed 64 MiB device array of the library
+ * instead of a caller workspace.  The call allocates nothing.
+ *
+ * Each device the library runs on holds one such array until the process
+ * ends, and every call on that device shares it: calls that overlap on one
+ * device (other streams, other host threads) race and give undefined
+ * results; calls ordered on one stream are safe.  The array needs no
+ * clearing (every partial a call reads was written by that call).
+ * Arguments as for qsa_sparse_attn_decode, without the workspace.
+ * Errors as for qsa_sparse_attn_decode; sizes whose partials exceed 64 MiB
+ * (qsa_sparse_attn_decode_workspace(...) > 64 MiB) -> QSA_ERR_WORKSPACE.
+ */
+qsa_status qsa_sparse_attn_decode_noalloc(const qsa_params* p, qsa_dtype dtype, const void* q,
+                                          const void* k_cache, const void* v_cache,
+                                          int64_t n_cap, const int32_t* d_seq_len,
+                                          const int32_t* idx, const int32_t* cnt, int32_t B,
+                                          int32_t n_q, int32_t hq, int32_t hkv, int32_t d,
+                                          float scale, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -261,6 +261,45 @@ qsa_status qsa_sparse_attn_decode(const qsa_params* p, qsa_dtype dtype, const vo
                   "sparse_attn_decode");
 }
 
+qsa_status qsa_sparse_attn_decode_noalloc(const qsa_params* p, qsa_dtype dtype, const void* q,
+                                          const void* k_cache, const void* v_cache,
+                                          int64_t n_cap, const int32_t* d_seq_len,
+                                          const int32_t* idx, const int32_t* cnt, int32_t B,
+                                          int32_t n_q, int32_t hq, int32_t hkv, int32_t d,
+                                          float scale, void* out, void* stream) {
+  qsa_status s = check_attn(p, dtype, q, k_cache, v_cache, idx, cnt, out, B, n_q, hq, hkv, d,
+                            n_cap);
+  if (s) return s;
+  if (!d_seq_len) return fail(QSA_ERR_NULL, "d_seq_len is NULL");
+  if (B == 0) return QSA_OK;
+  const size_t need = qsa_sparse_attn_decode_workspace(p, B, n_q, hq, hkv, d);
+  if (need > kDecodeScratchBytes)
+    return fail(QSA_ERR_WORKSPACE, "needs %zu bytes of scratch, beyond the fixed %zu", need,
+                kDecodeScratchBytes);
+  void* ws = nullptr;
+  hipError_t e = attn_static_scratch(&ws);
+  if (e != hipSuccess) return launched(e, "sparse_attn_decode_noalloc: scratch lookup");
+  AttnArgs a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.out = out;
+  a.idx = idx;
+  a.cnt = cnt;
+  a.seq_len = d_seq_len;
+  a.n_cap = n_cap;
+  a.q_pos0 = 0;
+  a.B = B;
+  a.n_q = n_q;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.kB = qsa_k_blocks(p);
+  a.r = p->r;
+  a.scale = scale > 0.f ? scale : 1.f / sqrtf((float)d);
+  return launched(launch_attn_decode(dtype, a, ws, (hipStream_t)stream),
+                  "sparse_attn_decode_noalloc");
+}
+
 qsa_status qsa_probe_gather(const qsa_params* p, const void* k, const void* v, int64_t n_cap,
                             const int32_t* idx, const int32_t* cnt, int32_t B, int32_t n_q,
                             int64_t q_pos0, int32_t hkv, int32_t waves_per_cu, int32_t depth,

@@ -19,6 +19,8 @@
 // partial (max, sum, unnormalised output) that attn_combine merges.
 #include <math.h>
 
+#include <mutex>
+
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -639,6 +641,35 @@ hipError_t launch_attn_prefill(qsa_dtype dt, const AttnArgs& a, hipStream_t st) 
 
 size_t attn_decode_workspace(int B, int n_q, int hkv, int kB) {
   return (size_t)B * n_q * hkv * decode_splits(kB) * kPartFloats * sizeof(float);
+}
+
+// ---- fixed scratch for the allocation-free decode entry point -------------
+// Each device that runs the library holds one copy of this array until the
+// process ends; its address on the current device is looked up once per
+// device (hipGetSymbolAddress) and kept.  Host code never passes the array's
+// name to a kernel: only the looked-up device address.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t attn_static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_attn_decode(qsa_dtype dt, const AttnArgs& a, void* ws, hipStream_t st) {

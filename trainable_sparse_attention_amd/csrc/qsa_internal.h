@@ -114,6 +114,12 @@ struct AttnArgs {
 hipError_t launch_attn_prefill(qsa_dtype dt, const AttnArgs& a, hipStream_t st);
 size_t attn_decode_workspace(int B, int n_q, int hkv, int kB);
 hipError_t launch_attn_decode(qsa_dtype dt, const AttnArgs& a, void* ws, hipStream_t st);
+// Size of the fixed device array behind qsa_sparse_attn_decode_noalloc: the
+// split partials of up to 8066 (sequence, new token, KV head, split) slots,
+// e.g. 8 sequences x 4 new tokens x 2 KV heads at k_B = 512 (65 splits).
+constexpr size_t kDecodeScratchBytes = (size_t)64 << 20;
+// This device's address of that array (looked up once per device).
+hipError_t attn_static_scratch(void** out);
 hipError_t launch_probe_gather(const AttnArgs& a, int waves_per_cu, int depth, int rg,
                                uint32_t* sink, hipStream_t st);
 

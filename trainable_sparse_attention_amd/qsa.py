@@ -20,7 +20,8 @@ STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL", 2: "QSA_ERR_SHAPE", 3: "QSA_ERR_DTYPE"
 EXPORTS = ["qsa_default_params", "qsa_k_blocks", "qsa_status_str", "qsa_last_error",
            "qsa_pool_keys", "qsa_index_topk", "qsa_index_topk_workspace",
            "qsa_sparse_attn_prefill", "qsa_sparse_attn_decode",
-           "qsa_sparse_attn_decode_workspace", "qsa_probe_gather"]
+           "qsa_sparse_attn_decode_workspace", "qsa_sparse_attn_decode_noalloc",
+           "qsa_probe_gather"]
 
 
 class QSAError(RuntimeError):
@@ -72,6 +73,9 @@ def lib():
         L.qsa_sparse_attn_decode.restype = ctypes.c_int
         L.qsa_sparse_attn_decode_workspace.argtypes = [PP, I32, I32, I32, I32, I32]
         L.qsa_sparse_attn_decode_workspace.restype = SZ
+        L.qsa_sparse_attn_decode_noalloc.argtypes = [PP, ctypes.c_int, P, P, P, I64, P, P, P,
+                                                     I32, I32, I32, I32, I32, F, P, P]
+        L.qsa_sparse_attn_decode_noalloc.restype = ctypes.c_int
         L.qsa_probe_gather.argtypes = [PP, P, P, I64, P, P, I32, I32, I64, I32, I32, I32, I32, P,
                                        P]
         L.qsa_probe_gather.restype = ctypes.c_int
@@ -159,6 +163,17 @@ def qsa_sparse_attn_decode(p, q, k_cache, v_cache, seq_len, idx, cnt, out, works
                                         B, n_q, hq, hkv, d, scale, _ptr(out), _ptr(workspace),
                                         0 if workspace is None else workspace.numel(),
                                         _stream(stream)))
+
+
+def qsa_sparse_attn_decode_noalloc(p, q, k_cache, v_cache, seq_len, idx, cnt, out, scale=0.0,
+                                   stream=None):
+    """qsa_sparse_attn_decode with the library's fixed scratch (no workspace)."""
+    B, n_q, hq, d = q.shape
+    hkv, n_cap = k_cache.shape[1], k_cache.shape[2]
+    _check(lib().qsa_sparse_attn_decode_noalloc(ctypes.byref(p), dtype_code(q), _ptr(q),
+                                                _ptr(k_cache), _ptr(v_cache), n_cap,
+                                                _ptr(seq_len), _ptr(idx), _ptr(cnt), B, n_q, hq,
+                                                hkv, d, scale, _ptr(out), _stream(stream)))
 
 
 def qsa_probe_gather(p, k, v, idx, cnt, sink, waves_per_cu=8, depth=1, rows_per_wave=1,
