@@ -252,7 +252,10 @@ def probe_sweep(torch, qsa, p, d, idx, cnt, flush, stream):
     return pts
 
 
-def bench_decode(name, args, torch, qsa, inputs, flush):
+def bench_decode(name, args, torch, qsa, inputs, flush, shared=False):
+    """One decode step per sequence batch: pool the blocks the new tokens
+    complete, select, attend.  shared: the step's new tokens share the one
+    selection made at the first new token (index reuse)."""
     d = inputs.make(name, seed=4, backend="torch")
     p = qsa.params()
     B, L, n_q, hq, hkv = d["B"], d["n"], d["n_q"], d["hq"], d["hkv"]
@@ -262,20 +265,24 @@ def bench_decode(name, args, torch, qsa, inputs, flush):
     kbar = torch.empty((B, nb, 128), dtype=d["k_idx"].dtype, device=dev)
     qsa.qsa_pool_keys(p, d["k_idx"], kbar, 0, nb)
     seq_len = torch.full((B,), L, dtype=torch.int32, device=dev)
-    idx = torch.empty((B, n_q, kB), dtype=torch.int32, device=dev)
-    cnt = torch.empty((B, n_q), dtype=torch.int32, device=dev)
+    n_sel = 1 if shared else n_q
+    # a shared selection is made for the first new token: its lengths end there
+    sel_len = torch.full((B,), L - n_q + 1, dtype=torch.int32, device=dev) if shared else seq_len
+    q_idx_sel = d["q_idx"][:, :1].contiguous() if shared else d["q_idx"]
+    idx = torch.empty((B, n_sel, kB), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, n_sel), dtype=torch.int32, device=dev)
     out = torch.empty_like(d["q"])
-    ws_i = qsa.workspace(qsa.qsa_index_topk_workspace(p, qsa.dtype_code(d["q_idx"]), B, n_q, nb,
-                                                      True))
+    ws_i = qsa.workspace(qsa.qsa_index_topk_workspace(p, qsa.dtype_code(d["q_idx"]), B, n_sel,
+                                                      nb, True))
     ws_a = qsa.workspace(qsa.qsa_sparse_attn_decode_workspace(p, B, n_q, hq, hkv))
     stream = torch.cuda.current_stream()
     # the blocks the new tokens complete are pooled into the cache
     b0, b1 = (L - n_q) // p.r, L // p.r
     # calls go to the current stream: the capture stream under a graph
+    attend = qsa.qsa_sparse_attn_decode_shared if shared else qsa.qsa_sparse_attn_decode
     stages = [lambda: qsa.qsa_pool_keys(p, d["k_idx"], kbar, b0, b1),
-              lambda: qsa.qsa_index_topk(p, d["q_idx"], kbar, idx, cnt, ws_i, 0, seq_len),
-              lambda: qsa.qsa_sparse_attn_decode(p, d["q"], d["k"], d["v"], seq_len, idx, cnt,
-                                                 out, ws_a, 0.0)]
+              lambda: qsa.qsa_index_topk(p, q_idx_sel, kbar, idx, cnt, ws_i, 0, sel_len),
+              lambda: attend(p, d["q"], d["k"], d["v"], seq_len, idx, cnt, out, ws_a, 0.0)]
     for _ in range(args.warmup):
         for f in stages:
             f()
@@ -302,14 +309,18 @@ def bench_decode(name, args, torch, qsa, inputs, flush):
     ms_u, _ = time_steps(torch, stream, [g.replay], K, lambda: None)
     c = cnt.to(torch.int64)
     pos = L - n_q + torch.arange(n_q, device=dev, dtype=torch.int64)
-    tails = int(((pos + 1) % p.r).sum().item()) * B
-    slots = int(c.sum().item()) * p.r + tails
+    if shared:  # each token: the shared blocks + tokens from the first token's block edge
+        start = (L - n_q + 1) // p.r * p.r
+        slots = int(c.sum().item()) * p.r * n_q + int((pos + 1 - start).sum().item()) * B
+    else:
+        tails = int(((pos + 1) % p.r).sum().item()) * B
+        slots = int(c.sum().item()) * p.r + tails
     elt = 2
     scan_bytes = B * nb * 128 * elt + B * n_q * nb * 4  # pooled keys once + scores
     gather_bytes = hkv * 2 * 128 * elt * slots
     io_bytes = B * n_q * (2 * hq * 128 * elt + 4 * 128 * elt + kB * 4)
     step_bytes = B * nb * 128 * elt + gather_bytes + io_bytes
-    return dict(name=name, B=B, L=L, n_q=n_q, ms=ms, ms_unflushed=ms_u, eager_ms=eager_ms,
+    return dict(name=name + ("_shared" if shared else ""), base=name, B=B, L=L, n_q=n_q, ms=ms, ms_unflushed=ms_u, eager_ms=eager_ms,
                 stage_ms=st, tok_s=B * n_q / (ms * 1e-3), step_bytes=step_bytes,
                 scan_bytes=scan_bytes, gather_bytes=gather_bytes,
                 step_gbs=step_bytes / (ms * 1e-3) / 1e9,
@@ -319,7 +330,9 @@ def bench_decode(name, args, torch, qsa, inputs, flush):
 def decode_record(inputs, dec, steps):
     return {
         "value": dec["tok_s"], "unit": "tokens/s", "ms_per_step": dec["ms"],
-        "steps": steps, "workload": inputs.describe(dec["name"]),
+        "steps": steps, "workload": inputs.describe(dec["base"]) + (
+            "; the new tokens share one selection made at the first (index reuse)"
+            if dec["name"] != dec["base"] else ""),
         "timing": "one HIP graph replay per step (the three calls captured once), "
                   "untimed 512 MB read before each step",
         "ms_per_step_unflushed": dec["ms_unflushed"],
@@ -402,10 +415,13 @@ def main():
     decs = []
     if not args.no_decode:
         names = [args.decode_cfg] + [x for x in args.more_decode.split(",") if x]
-        for name in names:
-            dec = bench_decode(name, args, torch, qsa, inputs, flush)
+        runs = [(x, False) for x in names] + [(x, True) for x in names
+                                              if inputs.CONFIGS[x].get("n_new", 1) > 1]
+        for name, shared in runs:
+            dec = bench_decode(name, args, torch, qsa, inputs, flush, shared)
             log("decode %s: %.4f ms/step as a graph replay (unflushed %.4f); eager %.4f ms/step "
-                "(pool %.4f, index %.4f, attn %.4f ms)" % (name, dec["ms"], dec["ms_unflushed"],
+                "(pool %.4f, index %.4f, attn %.4f ms)" % (dec["name"], dec["ms"],
+                                                           dec["ms_unflushed"],
                                                            dec["eager_ms"], *dec["stage_ms"]))
             decs.append(dec)
             torch.cuda.empty_cache()

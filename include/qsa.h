@@ -183,8 +183,39 @@ qsa_status qsa_sparse_attn_decode(const qsa_params* p, qsa_dtype dtype, const vo
                                   int32_t hkv, int32_t d, float scale, void* out,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes of qsa_sparse_attn_decode and qsa_sparse_attn_decode_shared
+ * for these sizes (the same for both calls). */
 size_t qsa_sparse_attn_decode_workspace(const qsa_params* p, int32_t B, int32_t n_q, int32_t hq,
                                         int32_t hkv, int32_t d);
+
+/*
+ * qsa_sparse_attn_decode_shared -- decode attention for n_q new tokens per
+ * sequence that share ONE block selection ([glide] "QSA Ablations and
+ * Efficiency": reusing the top-k indices across speculative decoding steps
+ * leaves the accepted length unchanged, Table 4; Figure 1: the MTP module
+ * reuses QSA indices across speculative steps).
+ *
+ * The selection is the one made for the step's first new token, at
+ * position f = d_seq_len[b] - n_q: idx[b][0][..cnt[b][0]] from
+ * qsa_index_topk with one query per sequence at that position (decode form
+ * with lengths d_seq_len[b] - n_q + 1).  New token t (position f + t)
+ * attends to the tokens of those blocks plus every token from
+ * floor((f+1)/r)*r to f + t: its own incomplete block and, for the later
+ * tokens, the blocks completed since the first token (which the shared
+ * selection could not score).  Every selected block is complete at f, so
+ * the set is causal for every token.
+ *
+ *   q : [B][n_q][hq][d]; caches [B][hkv][n_cap][d]; d_seq_len : device
+ *   int32 [B] (includes the new tokens); idx : [B][1][k_B]; cnt : [B][1];
+ *   out : [B][n_q][hq][d]; workspace : qsa_sparse_attn_decode_workspace
+ * Errors as for qsa_sparse_attn_decode.
+ */
+qsa_status qsa_sparse_attn_decode_shared(const qsa_params* p, qsa_dtype dtype, const void* q,
+                                         const void* k_cache, const void* v_cache, int64_t n_cap,
+                                         const int32_t* d_seq_len, const int32_t* idx,
+                                         const int32_t* cnt, int32_t B, int32_t n_q, int32_t hq,
+                                         int32_t hkv, int32_t d, float scale, void* out,
+                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * qsa_sparse_attn_decode_noalloc -- qsa_sparse_attn_decode for callers that

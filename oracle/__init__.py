@@ -20,4 +20,5 @@ from .oracle import (  # noqa: F401
     index_at,
     score_at,
     attend_at,
+    attend_shared,
 )

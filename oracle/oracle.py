@@ -55,6 +55,8 @@ def load():
         lib.orc_score_rows.restype = None
         lib.orc_attend_rows.argtypes = [P, P, P, I, L, L, P, L, P, P, I, I, I, I, I, D, P]
         lib.orc_attend_rows.restype = None
+        lib.orc_attend_shared.argtypes = [P, P, P, I, L, L, L, P, I, I, I, I, I, D, P]
+        lib.orc_attend_shared.restype = L
         lib.orc_index_at.argtypes = [P, P, I, I, I, I, I, D, I, P, L, P, P]
         lib.orc_index_at.restype = None
         lib.orc_score_at.argtypes = [P, P, I, I, I, I, I, D, P, L, P, L]
@@ -260,4 +262,29 @@ def attend_at(q_rows, k, v, pos, idx, cnt, r=4, scale=None):
     out = np.empty((m, hq, D), dtype=np.float64)
     load().orc_attend_at(_p(q_rows), _p(k), _p(v), dt, n_cap, _p(pos), m, _p(idx), _p(cnt), kB,
                          r, hq, hkv, D, float(scale), _p(out))
+    return out
+
+
+def attend_shared(q_rows, k, v, f, pos, idx_row, cnt, r=4, scale=None):
+    """Attention (float64 [m][hq][D]) of a decode step's new tokens that
+    share one selection made at position f: row u sits at pos[u] >= f and
+    attends to the selected blocks (idx_row[:cnt]) and to the tokens
+    floor((f+1)/r)*r .. pos[u].  q_rows [m][hq][D]; k, v [hkv][n_cap][D]."""
+    q_rows, k, v = _c(q_rows), _c(k), _c(v)
+    dt = _dt(q_rows, k, v)
+    m, hq, D = q_rows.shape
+    hkv, n_cap, _ = k.shape
+    idx_row = _c(np.asarray(idx_row, dtype=np.int32))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = np.empty((m, hq, D), dtype=np.float64)
+    step = hq * D * (2 if dt == BF16 else 4)
+    base = q_rows.ctypes.data
+    for u in range(m):
+        p_u = int(pos[u])
+        if p_u < f or p_u >= n_cap:
+            raise ValueError("positions must lie in [f, n_cap)")
+        load().orc_attend_shared(ctypes.c_void_p(base + u * step), _p(k), _p(v), dt, n_cap,
+                                 int(f), p_u, _p(idx_row), int(cnt), r, hq, hkv, D, float(scale),
+                                 out[u].ctypes.data_as(ctypes.c_void_p))
     return out

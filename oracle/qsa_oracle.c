@@ -193,24 +193,15 @@ int orc_select(const double* scores, int64_t nb, int kB, int32_t* idx_row) {
 }
 
 /*
- * Sparse core attention of one query ([glide] Figure 3: selected blocks are
- * expanded to token indices and joined with the incomplete-block tail; each
- * query attends only to that set).
- *   q_row: [hq][D]; k, v: [hkv][n_cap][D]; idx_row: cnt block ids.
- *   out: [hq][D] in double.  Returns |T_i|.
+ * Softmax attention of one query over an explicit token list ([glide]
+ * Figure 3: sparse core attention over the selected tokens).
+ *   q_row: [hq][D]; k, v: [hkv][n_cap][D]; tok: nT token rows.
+ *   out: [hq][D] in double.
  */
-int64_t orc_attend(const void* q_row, const void* k, const void* v, int dt, int64_t n_cap,
-                   int64_t pos, const int32_t* idx_row, int cnt, int r, int hq, int hkv,
-                   int D, double scale, double* out) {
-  int64_t nb = orc_nvis(pos, r);
-  int64_t ntail = pos + 1 - nb * r;
-  int64_t nT = (int64_t)cnt * r + ntail;
-  int64_t* tok = (int64_t*)malloc(sizeof(int64_t) * (size_t)nT);
-  double* w = (double*)malloc(sizeof(double) * (size_t)nT);
-  int64_t u = 0;
-  for (int s = 0; s < cnt; ++s)
-    for (int t = 0; t < r; ++t) tok[u++] = (int64_t)idx_row[s] * r + t;
-  for (int64_t t = nb * r; t <= pos; ++t) tok[u++] = t;
+static void orc_attend_list(const void* q_row, const void* k, const void* v, int dt,
+                            int64_t n_cap, const int64_t* tok, int64_t nT, int hq, int hkv, int D,
+                            double scale, double* out) {
+  double* w = (double*)malloc(sizeof(double) * (size_t)(nT > 0 ? nT : 1));
   for (int h = 0; h < hq; ++h) {
     int g = (int)(((int64_t)h * hkv) / hq);
     const int64_t kv0 = (int64_t)g * n_cap * D;
@@ -233,8 +224,53 @@ int64_t orc_attend(const void* q_row, const void* k, const void* v, int dt, int6
       out[(int64_t)h * D + c] = acc / z;
     }
   }
-  free(tok);
   free(w);
+}
+
+/*
+ * Sparse core attention of one query ([glide] Figure 3: selected blocks are
+ * expanded to token indices and joined with the incomplete-block tail; each
+ * query attends only to that set).
+ *   q_row: [hq][D]; k, v: [hkv][n_cap][D]; idx_row: cnt block ids.
+ *   out: [hq][D] in double.  Returns |T_i|.
+ */
+int64_t orc_attend(const void* q_row, const void* k, const void* v, int dt, int64_t n_cap,
+                   int64_t pos, const int32_t* idx_row, int cnt, int r, int hq, int hkv,
+                   int D, double scale, double* out) {
+  int64_t nb = orc_nvis(pos, r);
+  int64_t ntail = pos + 1 - nb * r;
+  int64_t nT = (int64_t)cnt * r + ntail;
+  int64_t* tok = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nT > 0 ? nT : 1));
+  int64_t u = 0;
+  for (int s = 0; s < cnt; ++s)
+    for (int t = 0; t < r; ++t) tok[u++] = (int64_t)idx_row[s] * r + t;
+  for (int64_t t = nb * r; t <= pos; ++t) tok[u++] = t;
+  orc_attend_list(q_row, k, v, dt, n_cap, tok, nT, hq, hkv, D, scale, out);
+  free(tok);
+  return nT;
+}
+
+/*
+ * Attention of one new token of a decode step whose new tokens share one
+ * block selection ([glide] "QSA Ablations and Efficiency": the top-k indices
+ * are reused across speculative decoding steps).  The selection (idx_row,
+ * cnt) was made at position f, the step's first new token; the token at
+ * position pos >= f attends to the selected blocks' tokens and to every
+ * token from floor((f+1)/r)*r to pos (its incomplete block and the blocks
+ * completed after f, which the selection could not score).  Returns |T|.
+ */
+int64_t orc_attend_shared(const void* q_row, const void* k, const void* v, int dt,
+                          int64_t n_cap, int64_t f, int64_t pos, const int32_t* idx_row, int cnt,
+                          int r, int hq, int hkv, int D, double scale, double* out) {
+  int64_t start = orc_nvis(f, r) * r;
+  int64_t nT = (int64_t)cnt * r + (pos + 1 - start);
+  int64_t* tok = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nT > 0 ? nT : 1));
+  int64_t u = 0;
+  for (int s = 0; s < cnt; ++s)
+    for (int t = 0; t < r; ++t) tok[u++] = (int64_t)idx_row[s] * r + t;
+  for (int64_t t = start; t <= pos; ++t) tok[u++] = t;
+  orc_attend_list(q_row, k, v, dt, n_cap, tok, nT, hq, hkv, D, scale, out);
+  free(tok);
   return nT;
 }
 

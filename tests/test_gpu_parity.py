@@ -274,6 +274,48 @@ def test_decode_parity(n_q, dtype, K, lens):
         assert rel_err(g_out[b], o) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("n_q,lens", [(4, (9000, 9001, 5003)), (4, (20003, 256, 4098)),
+                                      (2, (9002, 7000, 513))])
+def test_decode_shared_selection(n_q, lens):
+    """The pages' decode setting: n_q new tokens per sequence share the one
+    selection made at the first new token (index reuse across speculative
+    steps); each token attends to it plus every token from the first
+    token's block boundary up to its own position."""
+    say("decode shared selection n_q=%d lens=%s" % (n_q, lens))
+    lens = list(lens)
+    n = max(lens)
+    d = inputs.small(B=3, n=n, hq=16, hkv=2, dtype="bf16", seed=50 + n_q)
+    p = _params()
+    t = _dev_inputs(d)
+    kbar = _pool_gpu(p, t["k_idx"], n // 4)
+    seq_len = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    first_len = torch.tensor([L - n_q + 1 for L in lens], dtype=torch.int32, device="cuda")
+    qi = torch.stack([t["q_idx"][b, L - n_q:L - n_q + 1] for b, L in enumerate(lens)]).contiguous()
+    qq = torch.stack([t["q"][b, L - n_q:L] for b, L in enumerate(lens)]).contiguous()
+    idx, cnt = _index_gpu(p, qi, kbar, seq_len=first_len)
+    ws = qsa.workspace(qsa.qsa_sparse_attn_decode_workspace(p, 3, n_q, 16, 2))
+    out = torch.empty_like(qq)
+    qsa.qsa_sparse_attn_decode_shared(p, qq, t["k"], t["v"], seq_len, idx, cnt, out, ws)
+    # the first token alone through the ordinary decode call: same set, same bits
+    out1 = torch.empty_like(qq[:, :1])
+    ws1 = qsa.workspace(qsa.qsa_sparse_attn_decode_workspace(p, 3, 1, 16, 2))
+    qsa.qsa_sparse_attn_decode(p, qq[:, :1].contiguous(), t["k"], t["v"], first_len, idx, cnt,
+                               out1, ws1)
+    torch.cuda.synchronize()
+    assert torch.equal(out1[:, 0], out[:, 0])
+    kbar_h, g_idx, g_cnt, g_out = to_host(kbar), to_host(idx), to_host(cnt), to_host(out)
+    for b, L in enumerate(lens):
+        f = L - n_q
+        _check_index_at("shared seq %d" % b, d["q_idx"][b][[f]], kbar_h[b], np.array([f]),
+                        g_idx[b], g_cnt[b])
+        pos = np.arange(f, L)
+        o = oracle.attend_shared(d["q"][b][pos], d["k"][b], d["v"][b], f, pos, g_idx[b, 0],
+                                 g_cnt[b, 0])
+        err = rel_err(g_out[b], o)
+        say("shared seq", b, "attention rel err", err)
+        assert err <= TOL["bf16"]
+
+
 def test_decode_step_graph_replays():
     """A decode step (pool the newest block, index, attend) captured in a HIP
     graph: every replay, with eager work and synchronizations between the

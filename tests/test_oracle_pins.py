@@ -286,6 +286,63 @@ def test_masked_dense_equivalence():
     np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-13)
 
 
+# --------------------------------------------------------------------------
+# Index reuse across a decode step's new tokens ([glide] "QSA Ablations and
+# Efficiency": top-k indices reused across speculative decoding steps)
+# --------------------------------------------------------------------------
+
+def test_shared_selection_at_its_own_position_is_the_ordinary_rule():
+    n = 300
+    d = inputs.small(n=n, hq=8, hkv=2, r=4, K=32, seed=15)
+    kbar = oracle.pool(d["k_idx"][0])
+    for f in (130, 131, 132, 135):
+        idx, cnt = oracle.index_rows(d["q_idx"][0], kbar, [f], K=32)
+        a = oracle.attend_rows(d["q"][0], d["k"][0], d["v"][0], [f], idx, cnt)
+        b = oracle.attend_shared(d["q"][0][[f]], d["k"][0], d["v"][0], f, [f], idx[0], cnt[0])
+        np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("r", [4, 2])
+def test_shared_selection_with_every_block_is_dense_causal(r):
+    """K >= n: the first token selects every complete block, so each later
+    token attends to all of 0..pos -- torch's causal SDPA in float64."""
+    n, n_q = 41, 4
+    d = inputs.small(n=n, hq=8, hkv=2, r=r, K=4096, seed=16)
+    kbar = oracle.pool(d["k_idx"][0], r=r)
+    ref = _sdpa(d["q"][0], d["k"][0], d["v"][0], 8, 2, causal=True)
+    for f in (n - n_q, n - n_q - 1, n - n_q - 2):
+        idx, cnt = oracle.index_rows(d["q_idx"][0], kbar, [f], r=r, K=4096)
+        pos = np.arange(f, f + n_q)
+        out = oracle.attend_shared(d["q"][0][pos], d["k"][0], d["v"][0], f, pos, idx[0], cnt[0],
+                                   r=r)
+        np.testing.assert_allclose(out, ref[pos], rtol=1e-11, atol=1e-13)
+
+
+def test_shared_selection_masked_dense_equivalence():
+    """The shared token sets written as an explicit 0/1 mask (selected blocks
+    of the first token, then every token from its block boundary up to the
+    row) and run through masked SDPA: the same outputs, and the mask is
+    causal for every new token."""
+    n, r, K, n_q = 96, 4, 16, 4
+    d = inputs.small(n=n, hq=4, hkv=1, r=r, K=K, seed=17)
+    kbar = oracle.pool(d["k_idx"][0], r=r)
+    for f in (n - n_q, n - n_q - 2):
+        idx, cnt = oracle.index_rows(d["q_idx"][0], kbar, [f], r=r, K=K)
+        pos = np.arange(f, f + n_q)
+        mask = np.zeros((n, n), dtype=bool)
+        mask[np.arange(n), np.arange(n)] = True  # rows not checked: any valid mask
+        for p_ in pos:
+            mask[p_] = False
+            for b in idx[0, :cnt[0]]:
+                mask[p_, b * r:b * r + r] = True
+            mask[p_, (f + 1) // r * r:p_ + 1] = True
+        assert not np.any(np.triu(mask, 1)), "shared sets must be causal"
+        ref = _sdpa(d["q"][0], d["k"][0], d["v"][0], 4, 1, mask=mask)
+        out = oracle.attend_shared(d["q"][0][pos], d["k"][0], d["v"][0], f, pos, idx[0], cnt[0],
+                                   r=r)
+        np.testing.assert_allclose(out, ref[pos], rtol=1e-11, atol=1e-13)
+
+
 def test_attention_constant_values_and_first_token():
     n = 32
     d = inputs.small(n=n, hq=4, hkv=1, r=4, K=8, seed=11)

@@ -214,6 +214,7 @@ qsa_status qsa_sparse_attn_prefill(const qsa_params* p, qsa_dtype dtype, const v
   a.hkv = hkv;
   a.kB = qsa_k_blocks(p);
   a.r = p->r;
+  a.shared = 0;
   a.scale = scale > 0.f ? scale : 1.f / sqrtf((float)d);
   return launched(launch_attn_prefill(dtype, a, (hipStream_t)stream), "sparse_attn_prefill");
 }
@@ -223,7 +224,9 @@ size_t qsa_sparse_attn_decode_workspace(const qsa_params* p, int32_t B, int32_t 
   (void)hq;
   (void)d;
   if (!p || B <= 0 || n_q <= 0 || hkv <= 0) return 0;
-  return attn_decode_workspace(B, n_q, hkv, qsa_k_blocks(p));
+  // sized for either form of the decode call (a shared selection can add a
+  // tail slot)
+  return attn_decode_workspace(B, n_q, hkv, qsa_k_blocks(p), p->r, true);
 }
 
 qsa_status qsa_sparse_attn_decode(const qsa_params* p, qsa_dtype dtype, const void* q,
@@ -256,9 +259,46 @@ qsa_status qsa_sparse_attn_decode(const qsa_params* p, qsa_dtype dtype, const vo
   a.hkv = hkv;
   a.kB = qsa_k_blocks(p);
   a.r = p->r;
+  a.shared = 0;
   a.scale = scale > 0.f ? scale : 1.f / sqrtf((float)d);
   return launched(launch_attn_decode(dtype, a, workspace, (hipStream_t)stream),
                   "sparse_attn_decode");
+}
+
+qsa_status qsa_sparse_attn_decode_shared(const qsa_params* p, qsa_dtype dtype, const void* q,
+                                         const void* k_cache, const void* v_cache, int64_t n_cap,
+                                         const int32_t* d_seq_len, const int32_t* idx,
+                                         const int32_t* cnt, int32_t B, int32_t n_q, int32_t hq,
+                                         int32_t hkv, int32_t d, float scale, void* out,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  qsa_status s = check_attn(p, dtype, q, k_cache, v_cache, idx, cnt, out, B, n_q, hq, hkv, d,
+                            n_cap);
+  if (s) return s;
+  if (!d_seq_len) return fail(QSA_ERR_NULL, "d_seq_len is NULL");
+  if (B == 0) return QSA_OK;
+  const size_t need = qsa_sparse_attn_decode_workspace(p, B, n_q, hq, hkv, d);
+  if (!workspace || workspace_bytes < need)
+    return fail(QSA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  AttnArgs a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.out = out;
+  a.idx = idx;
+  a.cnt = cnt;
+  a.seq_len = d_seq_len;
+  a.n_cap = n_cap;
+  a.q_pos0 = 0;
+  a.B = B;
+  a.n_q = n_q;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.kB = qsa_k_blocks(p);
+  a.r = p->r;
+  a.shared = 1;
+  a.scale = scale > 0.f ? scale : 1.f / sqrtf((float)d);
+  return launched(launch_attn_decode(dtype, a, workspace, (hipStream_t)stream),
+                  "sparse_attn_decode_shared");
 }
 
 qsa_status qsa_sparse_attn_decode_noalloc(const qsa_params* p, qsa_dtype dtype, const void* q,
@@ -295,6 +335,7 @@ qsa_status qsa_sparse_attn_decode_noalloc(const qsa_params* p, qsa_dtype dtype, 
   a.hkv = hkv;
   a.kB = qsa_k_blocks(p);
   a.r = p->r;
+  a.shared = 0;
   a.scale = scale > 0.f ? scale : 1.f / sqrtf((float)d);
   return launched(launch_attn_decode(dtype, a, ws, (hipStream_t)stream),
                   "sparse_attn_decode_noalloc");
@@ -331,6 +372,7 @@ qsa_status qsa_probe_gather(const qsa_params* p, const void* k, const void* v, i
   a.hkv = hkv;
   a.kB = qsa_k_blocks(p);
   a.r = p->r;
+  a.shared = 0;
   a.scale = 1.f;
   return launched(launch_probe_gather(a, waves_per_cu, depth, rows_per_wave, sink,
                                       (hipStream_t)stream),

@@ -40,32 +40,45 @@ struct Row {
   const int32_t* ids;
 };
 
+// A row's token set: the cnt selected blocks, then the tail slots, which
+// hold the tokens nb*r .. pos (block nb + j is tail slot j).  Ordinarily nb
+// is the row's own complete-block count and the tail is its incomplete
+// block; when a decode step's new tokens share one selection (made at the
+// step's first new token), nb is the first token's count, so a later token's
+// tail also covers the blocks completed since.
 __device__ __forceinline__ Row row_ctx(const AttnArgs& a, int b, int t) {
   Row R;
   R.pos = a.seq_len ? (int64_t)a.seq_len[b] - a.n_q + t : a.q_pos0 + t;
-  R.nb = (R.pos + 1) / a.r;
+  const int ts = a.shared ? 0 : t;  // row of the selection this token uses
+  const int64_t psel = a.shared ? R.pos - t : R.pos;
+  R.nb = (psel + 1) / a.r;
   R.ntail = (int)(R.pos + 1 - R.nb * a.r);
-  R.cnt = a.cnt[(int64_t)b * a.n_q + t];
-  R.nslots = R.cnt + (R.ntail > 0 ? 1 : 0);
-  R.ids = a.idx + ((int64_t)b * a.n_q + t) * a.kB;
+  const int nsel = a.shared ? 1 : a.n_q;
+  R.cnt = a.cnt[(int64_t)b * nsel + ts];
+  R.nslots = R.cnt + (R.ntail + a.r - 1) / a.r;
+  R.ids = a.idx + ((int64_t)b * nsel + ts) * a.kB;
   return R;
+}
+
+// Tokens of slot u (< nslots) in the token set: r for a selected block, the
+// rest of the tail for a tail slot.
+__device__ __forceinline__ int slot_tokens(const Row& R, int u, int r) {
+  return u < R.cnt ? r : min(r, R.ntail - (u - R.cnt) * r);
+}
+// Block of slot u (< nslots).
+__device__ __forceinline__ int64_t slot_block(const Row& R, int u) {
+  return u < R.cnt ? (int64_t)R.ids[u] : R.nb + (u - R.cnt);
 }
 
 // Token row of key `tok` (< r) of slot u; false if the key is not in T_i.
 __device__ __forceinline__ bool slot_row(const Row& R, int u, int s1, int tok, int r,
                                          int64_t* row) {
-  if (u >= s1) {
+  if (u >= s1 || tok >= slot_tokens(R, u, r)) {
     *row = 0;
     return false;
   }
-  if (u < R.cnt) {
-    *row = (int64_t)R.ids[u] * r + tok;
-    return true;
-  }
-  *row = R.nb * r + tok;  // tail slot
-  const bool ok = tok < R.ntail;
-  if (!ok) *row = 0;
-  return ok;
+  *row = slot_block(R, u) * r + tok;
+  return true;
 }
 
 __device__ __forceinline__ float wave_max_xor(float x) {
@@ -145,7 +158,7 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
   auto fill_ids = [&](int b0) {
     for (int u = lane; u < fill_n; u += 64) {
       const int sl = b0 + u;
-      ids[u] = sl < R.cnt ? R.ids[sl] : (sl < s1 ? (int)R.nb : 0);
+      ids[u] = sl < s1 ? (int)slot_block(R, sl) : 0;
     }
   };
   fill_ids(base);
@@ -153,7 +166,7 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
   // Token row of key tok of slot u with block id `id`, 0 if the key is not
   // in T_i (branch-free).
   auto row_sel = [&](int u, int id, int tok) -> uint32_t {
-    const bool ok = u < s1 && (u < R.cnt || tok < R.ntail);
+    const bool ok = u < s1 && tok < slot_tokens(R, u, a.r);
     return ok ? (uint32_t)id * (uint32_t)a.r + (uint32_t)tok : 0u;
   };
   const int G = a.hq / a.hkv;
@@ -260,7 +273,7 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
     for (int kt = 0; kt < 2; ++kt) {
       const int u = s + 4 * kt + gq;
       const bool slot_ok = u < s1;
-      const int ntok = u < R.cnt ? a.r : R.ntail;
+      const int ntok = slot_ok ? slot_tokens(R, u, a.r) : 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         sv[4 * kt + i] = (slot_ok && i < ntok) ? sacc[kt][i] * sl2 : -INFINITY;
@@ -619,14 +632,22 @@ static int resident_waves() {
   return res_cached;
 }
 
-static int decode_splits(int kB) { return (kB + 1 + kSlotsPerChunk - 1) / kSlotsPerChunk; }
+// Tail slots a row can have: its incomplete block, and with a shared
+// selection the blocks completed by the step's later tokens as well.
+static int max_tail_slots(int r, int n_q, bool shared) {
+  const int tail = r - 1 + (shared ? n_q - 1 : 0);
+  return (tail + r - 1) / r;
+}
+static int decode_splits(int kB, int r, int n_q, bool shared) {
+  return (kB + max_tail_slots(r, n_q, shared) + kSlotsPerChunk - 1) / kSlotsPerChunk;
+}
 
 hipError_t launch_attn_prefill(qsa_dtype dt, const AttnArgs& a, hipStream_t st) {
   const int64_t waves = (int64_t)a.B * a.n_q * a.hkv;
   if (waves == 0) return hipSuccess;
   if (dt == QSA_BF16) {
     // every slot id fits one window
-    if (a.kB + 1 + kSlotsPerChunk <= kIdWin)
+    if (a.kB + max_tail_slots(a.r, a.n_q, a.shared) + kSlotsPerChunk <= kIdWin)
       hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3((unsigned)waves), dim3(64),
                          bf16_lds_prefill(), st, a, 1, (float*)nullptr, resident_waves());
     else
@@ -639,8 +660,8 @@ hipError_t launch_attn_prefill(qsa_dtype dt, const AttnArgs& a, hipStream_t st) 
   return hipGetLastError();
 }
 
-size_t attn_decode_workspace(int B, int n_q, int hkv, int kB) {
-  return (size_t)B * n_q * hkv * decode_splits(kB) * kPartFloats * sizeof(float);
+size_t attn_decode_workspace(int B, int n_q, int hkv, int kB, int r, bool shared) {
+  return (size_t)B * n_q * hkv * decode_splits(kB, r, n_q, shared) * kPartFloats * sizeof(float);
 }
 
 // ---- fixed scratch for the allocation-free decode entry point -------------
@@ -673,7 +694,7 @@ hipError_t attn_static_scratch(void** out) {
 }
 
 hipError_t launch_attn_decode(qsa_dtype dt, const AttnArgs& a, void* ws, hipStream_t st) {
-  const int nsplit = decode_splits(a.kB);
+  const int nsplit = decode_splits(a.kB, a.r, a.n_q, a.shared);
   const int64_t waves = (int64_t)a.B * a.n_q * a.hkv * nsplit;
   if (waves == 0) return hipSuccess;
   float* part = (float*)ws;

@@ -108,11 +108,14 @@ struct AttnArgs {
   int64_t n_cap;
   int64_t q_pos0;
   int B, n_q, hq, hkv, kB, r;
+  // decode: the n_q new tokens of a sequence share the one selection idx[b][0]
+  // made at the first new token (its tail then runs from that token's block)
+  int shared;
   float scale;
 };
 
 hipError_t launch_attn_prefill(qsa_dtype dt, const AttnArgs& a, hipStream_t st);
-size_t attn_decode_workspace(int B, int n_q, int hkv, int kB);
+size_t attn_decode_workspace(int B, int n_q, int hkv, int kB, int r, bool shared);
 hipError_t launch_attn_decode(qsa_dtype dt, const AttnArgs& a, void* ws, hipStream_t st);
 // Size of the fixed device array behind qsa_sparse_attn_decode_noalloc: the
 // split partials of up to 8066 (sequence, new token, KV head, split) slots,

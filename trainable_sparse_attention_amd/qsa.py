@@ -20,7 +20,8 @@ STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL", 2: "QSA_ERR_SHAPE", 3: "QSA_ERR_DTYPE"
 EXPORTS = ["qsa_default_params", "qsa_k_blocks", "qsa_status_str", "qsa_last_error",
            "qsa_pool_keys", "qsa_index_topk", "qsa_index_topk_workspace",
            "qsa_sparse_attn_prefill", "qsa_sparse_attn_decode",
-           "qsa_sparse_attn_decode_workspace", "qsa_sparse_attn_decode_noalloc",
+           "qsa_sparse_attn_decode_workspace", "qsa_sparse_attn_decode_shared",
+           "qsa_sparse_attn_decode_noalloc",
            "qsa_probe_gather"]
 
 
@@ -73,6 +74,9 @@ def lib():
         L.qsa_sparse_attn_decode.restype = ctypes.c_int
         L.qsa_sparse_attn_decode_workspace.argtypes = [PP, I32, I32, I32, I32, I32]
         L.qsa_sparse_attn_decode_workspace.restype = SZ
+        L.qsa_sparse_attn_decode_shared.argtypes = [PP, ctypes.c_int, P, P, P, I64, P, P, P, I32,
+                                                    I32, I32, I32, I32, F, P, P, SZ, P]
+        L.qsa_sparse_attn_decode_shared.restype = ctypes.c_int
         L.qsa_sparse_attn_decode_noalloc.argtypes = [PP, ctypes.c_int, P, P, P, I64, P, P, P,
                                                      I32, I32, I32, I32, I32, F, P, P]
         L.qsa_sparse_attn_decode_noalloc.restype = ctypes.c_int
@@ -163,6 +167,20 @@ def qsa_sparse_attn_decode(p, q, k_cache, v_cache, seq_len, idx, cnt, out, works
                                         B, n_q, hq, hkv, d, scale, _ptr(out), _ptr(workspace),
                                         0 if workspace is None else workspace.numel(),
                                         _stream(stream)))
+
+
+def qsa_sparse_attn_decode_shared(p, q, k_cache, v_cache, seq_len, idx, cnt, out, workspace,
+                                  scale=0.0, stream=None):
+    """n_q new tokens per sequence sharing the selection idx [B][1][k_B] made
+    at the first new token (position seq_len[b] - n_q)."""
+    B, n_q, hq, d = q.shape
+    hkv, n_cap = k_cache.shape[1], k_cache.shape[2]
+    _check(lib().qsa_sparse_attn_decode_shared(ctypes.byref(p), dtype_code(q), _ptr(q),
+                                               _ptr(k_cache), _ptr(v_cache), n_cap, _ptr(seq_len),
+                                               _ptr(idx), _ptr(cnt), B, n_q, hq, hkv, d, scale,
+                                               _ptr(out), _ptr(workspace),
+                                               0 if workspace is None else workspace.numel(),
+                                               _stream(stream)))
 
 
 def qsa_sparse_attn_decode_noalloc(p, q, k_cache, v_cache, seq_len, idx, cnt, out, scale=0.0,
