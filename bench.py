@@ -69,8 +69,9 @@ def log(*a):
 
 
 class ClockSampler:
-    """Samples the graphics clock of device 0 (amdsmi) every few ms on a
-    host thread while the timed steps run; reports min / median / max MHz.
+    """Samples the graphics clock of device 0 (amdsmi metrics table, mean
+    over the XCDs) every few ms on a host thread while the timed steps run;
+    reports min / median / max MHz.
     Informative only: any failure is recorded, not raised."""
 
     def __init__(self):
@@ -93,8 +94,14 @@ class ClockSampler:
         def run():
             while not self._stop.is_set():
                 try:
-                    c = self._smi.amdsmi_get_clock_info(self._h, self._smi.AmdSmiClkType.GFX)
-                    self.vals.append(c.get("clk"))
+                    # per-XCD current graphics clocks from the metrics table
+                    m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+                    xs = [x for x in (m.get("current_gfxclks") or [])
+                          if isinstance(x, (int, float)) and 0 < x < 10000]
+                    if not xs and isinstance(m.get("current_gfxclk"), (int, float)):
+                        xs = [m["current_gfxclk"]]
+                    if xs:
+                        self.vals.append(sum(xs) / len(xs))
                 except Exception as e:
                     self.err = str(e)[:120]
                     return

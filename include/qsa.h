@@ -38,7 +38,7 @@
  *     in the caches).  Block b is visible to position p iff (b+1)r-1 <= p.
  *   - Inputs must be finite; NaN or Inf give undefined selections.
  *   - Results are deterministic: identical inputs give identical bits.
- *   - Supported shapes: r = 4, h_idx = 4, d_idx = 128, rope_dims even and
+ *   - Supported shapes: r in {1, 2, 4, 8, 16}, h_idx = 4, d_idx = 128, rope_dims even and
  *     <= 128, K >= r, head dim d = 128, hq % hkv == 0, hq / hkv <= 16;
  *     k_B = ceil(K/r) <= 3072 for qsa_index_topk over more than 4 query rows
  *     per sequence and <= 4096 for its decode form (at most 4 new tokens);
@@ -109,6 +109,24 @@ const char* qsa_last_error(void);
 qsa_status qsa_pool_keys(const qsa_params* p, qsa_dtype dtype, const void* k_idx, int64_t n_cap,
                          void* kbar, int64_t nb_cap, int32_t B, int64_t block_begin,
                          int64_t block_end, void* stream);
+
+/*
+ * qsa_pool_keys_rmsnorm -- qsa_pool_keys with the block mean RMS-normalised
+ * before the rotation ([glide] "Qwen Sparse Attention": the toy applies
+ * RMSNorm to the average-pooled keys; [hub]: the partial RoPE comes after
+ * the compression):
+ *
+ *   m = (1/r) sum_{t<r} k_idx[b][j*r+t],   y[c] = m[c] * gamma[c] / sqrt(mean_c(m^2) + eps)
+ *   kbar[b][j] = RoPE_{(j+1)r-1}(y), rounded (nearest-even) to dtype.
+ *
+ *   gamma : device float32 [d_idx], the learned gain;  eps >= 0
+ * Errors as for qsa_pool_keys; gamma NULL -> QSA_ERR_NULL; eps negative or
+ * not finite -> QSA_ERR_SHAPE.
+ */
+qsa_status qsa_pool_keys_rmsnorm(const qsa_params* p, qsa_dtype dtype, const void* k_idx,
+                                 int64_t n_cap, const float* gamma, float eps, void* kbar,
+                                 int64_t nb_cap, int32_t B, int64_t block_begin,
+                                 int64_t block_end, void* stream);
 
 /*
  * qsa_index_topk -- compressed MQA indexer and top-k_B block selection

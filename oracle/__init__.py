@@ -8,6 +8,7 @@ from .oracle import (  # noqa: F401
     build,
     load,
     pool,
+    pool_rmsnorm,
     rope_rows,
     scores,
     select,

@@ -43,6 +43,8 @@ def load():
         P, I, L, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
         lib.orc_pool.argtypes = [P, I, I, I, I, D, L, L, P, I]
         lib.orc_pool.restype = None
+        lib.orc_pool_rmsnorm.argtypes = [P, I, I, I, I, D, L, L, P, D, P, I]
+        lib.orc_pool_rmsnorm.restype = None
         lib.orc_rope_rows.argtypes = [P, L, I, I, D, P]
         lib.orc_rope_rows.restype = None
         lib.orc_scores.argtypes = [P, P, I, I, I, I, I, D, L, P]
@@ -103,6 +105,22 @@ def pool(k_idx, r=4, rope_dims=64, theta=10000.0, b0=0, b1=None):
         b1 = n // r
     out = np.empty((b1 - b0, d), dtype=k_idx.dtype)
     load().orc_pool(_p(k_idx), dt, d, r, rope_dims, float(theta), b0, b1, _p(out), dt)
+    return out
+
+
+def pool_rmsnorm(k_idx, gamma, eps=1e-6, r=4, rope_dims=64, theta=10000.0, b0=0, b1=None):
+    """Pooled keys of blocks [b0, b1) with the block mean RMS-normalised (gain
+    gamma [d], float64) before the rotation; same storage type as k_idx."""
+    k_idx = _c(k_idx)
+    dt = _dt(k_idx)
+    n, d = k_idx.shape
+    if b1 is None:
+        b1 = n // r
+    g = _c(np.asarray(gamma, dtype=np.float64))
+    assert g.shape == (d,)
+    out = np.empty((b1 - b0, d), dtype=k_idx.dtype)
+    load().orc_pool_rmsnorm(_p(k_idx), dt, d, r, rope_dims, float(theta), b0, b1, _p(g),
+                            float(eps), _p(out), dt)
     return out
 
 

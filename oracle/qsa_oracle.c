@@ -124,6 +124,33 @@ void orc_pool(const void* k_idx, int dt_in, int d, int r, int R, double theta,
 }
 
 /*
+ * Pool keys of blocks [b0, b1) with the block mean RMS-normalised before the
+ * rotation ([glide] "Qwen Sparse Attention": the toy average-pools the keys
+ * and applies RMSNorm to obtain the compressed keys; [hub]: partial RoPE
+ * after the compression):  y_c = m_c * gamma_c / sqrt((1/d) sum_c m_c^2 + eps).
+ *   gamma: [d] gain (double); kbar_out: [(b1-b0)][d] in dtype dt_out.
+ */
+void orc_pool_rmsnorm(const void* k_idx, int dt_in, int d, int r, int R, double theta,
+                      int64_t b0, int64_t b1, const double* gamma, double eps, void* kbar_out,
+                      int dt_out) {
+  double* m = (double*)malloc(sizeof(double) * (size_t)d);
+  for (int64_t b = b0; b < b1; ++b) {
+    double ss = 0.0;
+    for (int c = 0; c < d; ++c) {
+      double s = 0.0;
+      for (int t = 0; t < r; ++t) s += orc_ld(k_idx, dt_in, (b * r + t) * (int64_t)d + c);
+      m[c] = s / (double)r;
+      ss += m[c] * m[c];
+    }
+    double inv = 1.0 / sqrt(ss / (double)d + eps);
+    for (int c = 0; c < d; ++c) m[c] = m[c] * gamma[c] * inv;
+    orc_rope(m, R, theta, (double)((b + 1) * r - 1));
+    for (int c = 0; c < d; ++c) orc_st(kbar_out, dt_out, (b - b0) * (int64_t)d + c, m[c]);
+  }
+  free(m);
+}
+
+/*
  * Block scores of one query ([hub] I_ib = sum_h ReLU(<q_i^h, kbar_b>), MQA:
  * h_idx query heads against one shared key head; [glide] the compressed
  * causal mask: token i scores only the blocks complete by i).

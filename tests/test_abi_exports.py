@@ -56,8 +56,17 @@ def test_host_validation_errors():
     _expect(lib.qsa_pool_keys(P, 1, fake, 60, fake, 16, 1, 0, 16, None), 2, lib)
     _expect(lib.qsa_pool_keys(P, 1, fake, 64, fake, 15, 1, 0, 16, None), 2, lib)
     _expect(lib.qsa_pool_keys(P, 1, fake, 64, fake, 16, 1, 5, 4, None), 2, lib)
-    bad = qsa.params(r=8)
-    _expect(lib.qsa_pool_keys(ctypes.byref(bad), 1, fake, 64, fake, 16, 1, 0, 8, None), 4, lib)
+    for r in (3, 32, 0):  # built for r in {1, 2, 4, 8, 16}
+        bad = qsa.params(r=r)
+        _expect(lib.qsa_pool_keys(ctypes.byref(bad), 1, fake, 64, fake, 16, 1, 0, 8, None), 4,
+                lib)
+    # RMS-normalised pooling: gain and eps checked
+    _expect(lib.qsa_pool_keys_rmsnorm(P, 1, fake, 64, None, 1e-6, fake, 16, 1, 0, 16, None), 1,
+            lib)
+    _expect(lib.qsa_pool_keys_rmsnorm(P, 1, fake, 64, fake, -1.0, fake, 16, 1, 0, 16, None), 2,
+            lib)
+    _expect(lib.qsa_pool_keys_rmsnorm(P, 1, fake, 60, fake, 1e-6, fake, 16, 1, 0, 16, None), 2,
+            lib)
     _expect(lib.qsa_pool_keys(None, 1, fake, 64, fake, 16, 1, 0, 8, None), 1, lib)
     # index: too few blocks for the positions; workspace missing; n_q < 1
     _expect(lib.qsa_index_topk(P, 1, fake, fake, 10, 1, 64, 0, None, fake, fake, fake, 1 << 30,

@@ -128,6 +128,62 @@ def test_pool_parity(dtype):
         assert np.all(got[b, nb:] == 0), "rows beyond the range were written"
 
 
+def _assert_pooled_close(got, ref, dtype):
+    """The kernel normalises and rotates in float32, the oracle in float64
+    with one final rounding.  Bound: one ulp of the stored value plus the
+    float32 error of the normalise-and-rotate steps, a few 2^-24 of the
+    key's largest element (a rotated pair that nearly cancels can sit many
+    of its own bf16 ulps below that)."""
+    floor = 8 * 2.0 ** -24 * np.max(np.abs(ref), axis=1, keepdims=True)
+    if dtype == "bf16":
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+        bad = np.abs(got - ref) > ulp + floor
+    else:
+        bad = np.abs(got - ref) > floor
+    assert not np.any(bad), "pooled keys differ at %s" % (np.argwhere(bad)[:4].tolist(),)
+
+
+@pytest.mark.parametrize("dtype,r", [("bf16", 4), ("fp32", 4), ("bf16", 16), ("bf16", 1)])
+def test_pool_rmsnorm_parity(dtype, r):
+    """Pooled keys RMS-normalised with a gain before the rotation, at
+    positions up to 2^20 (blocks near the end of a 1M-token sequence are
+    pooled through a range offset), then the selection of a few rows."""
+    say("pool rmsnorm", dtype, r)
+    n = 6000
+    d = inputs.small(B=2, n=n, dtype=dtype, r=r, seed=23)
+    p = qsa.params(r=r)
+    nb = n // r
+    rng = np.random.default_rng(5)
+    gamma_h = rng.uniform(0.25, 2.0, 128).astype(np.float32)
+    gamma = torch.from_numpy(gamma_h).cuda()
+    k_idx = to_dev(d["k_idx"])
+    kbar = torch.zeros((2, nb, 128), dtype=k_idx.dtype, device="cuda")
+    qsa.qsa_pool_keys_rmsnorm(p, k_idx, gamma, 1e-6, kbar, 0, nb)
+    torch.cuda.synchronize()
+    got = to_host(kbar)
+    for b in range(2):
+        ref = as_f64(oracle.pool_rmsnorm(d["k_idx"][b], gamma_h.astype(np.float64), 1e-6, r=r))
+        _assert_pooled_close(as_f64(got[b]), ref, dtype)
+    # far positions: a sequence whose first 2^20 - 4096 tokens are absent
+    # (their blocks are never pooled) -- only the last blocks are pooled
+    big = (1 << 20) // r
+    kb2 = torch.zeros((1, big, 128), dtype=k_idx.dtype, device="cuda")
+    kfar = torch.zeros((1, big * r, 128), dtype=k_idx.dtype, device="cuda")
+    kfar[0, big * r - n:] = k_idx[0]
+    qsa.qsa_pool_keys_rmsnorm(p, kfar, gamma, 1e-6, kb2, big - nb, big)
+    torch.cuda.synchronize()
+    kfar_h = to_host(kfar[0])
+    ref = as_f64(oracle.pool_rmsnorm(kfar_h, gamma_h.astype(np.float64), 1e-6, r=r, b0=big - 64,
+                                     b1=big))
+    _assert_pooled_close(as_f64(to_host(kb2[0, big - 64:])), ref, dtype)
+    # the indexer consumes normalised keys like any others
+    idx, cnt = _index_gpu(p, to_dev(d["q_idx"]), kbar)
+    torch.cuda.synchronize()
+    rows = np.array([0, 3, n // 2, n - 5, n - 1])
+    if r == 4:
+        _check_index_rows(0, rows, to_host(idx), to_host(cnt), d["q_idx"][0], got[0], 2048)
+
+
 def test_prefill_4k_fp32_end_to_end_all_rows():
     """The 4K-token float32 workload (4 q heads / 1 kv head, 16 planted), every row."""
     say("4K fp32 end to end")
@@ -314,6 +370,95 @@ def test_decode_shared_selection(n_q, lens):
         err = rel_err(g_out[b], o)
         say("shared seq", b, "attention rel err", err)
         assert err <= TOL["bf16"]
+
+
+# ---- micro-block sizes other than 4 ([glide] "QSA Ablations and Efficiency",
+# Figure 5(a) and Figure 6(a,b) sweep the micro-block size / compression) ----
+
+def _transition_rows(n, kB, r, nrand=192, seed=3):
+    first = kB * r + r - 1  # first row that sees more than k_B blocks
+    rng = np.random.default_rng(seed)
+    rows = np.concatenate([np.arange(8), np.arange(first - 6, first + 6), rng.integers(0, n, nrand),
+                           np.arange(n - 8, n)])
+    return np.unique(rows[(rows >= 0) & (rows < n)]).astype(np.int64)
+
+
+@pytest.mark.parametrize("r,dtype,n", [(1, "bf16", 5003), (2, "bf16", 6001), (8, "bf16", 9001),
+                                       (16, "bf16", 20003), (2, "fp32", 3001),
+                                       (16, "fp32", 9000), (8, "bf16", 300)])
+def test_block_size_variants_prefill(r, dtype, n):
+    say("block size r=%d %s n=%d" % (r, dtype, n))
+    K = 2048
+    p = qsa.params(r=r, K=K)
+    kB = qsa.k_blocks(p)
+    d = inputs.small(B=2, n=n, hq=8, hkv=2, dtype=dtype, r=r, K=K, seed=200 + r,
+                     planted=8 if n > K + r else 0)
+    t = _dev_inputs(d)
+    nb = n // r
+    kbar = torch.zeros((2, max(nb, 1), 128), dtype=t["k_idx"].dtype, device="cuda")
+    if nb:
+        qsa.qsa_pool_keys(p, t["k_idx"], kbar, 0, nb)
+    idx, cnt = _index_gpu(p, t["q_idx"], kbar)
+    out = _attn_gpu(p, t["q"], t["k"], t["v"], idx, cnt)
+    torch.cuda.synchronize()
+    kbar_h, g_idx, g_cnt, g_out = to_host(kbar), to_host(idx), to_host(cnt), to_host(out)
+    rows = _transition_rows(n, kB, r)
+    for b in range(2):
+        if nb:
+            ref = as_f64(oracle.pool(d["k_idx"][b], r=r))
+            _assert_pooled_close(as_f64(kbar_h[b, :nb]), ref, dtype)
+        o_idx, o_cnt = oracle.index_rows(d["q_idx"][b], kbar_h[b], rows, r=r, K=K)
+        gi, gc = g_idx[b][rows], g_cnt[b][rows]
+        assert np.array_equal(gc, o_cnt), "counts differ"
+        differ = [u for u in range(len(rows)) if not np.array_equal(gi[u], o_idx[u])]
+        if differ:
+            sc = oracle.score_rows(d["q_idx"][b], kbar_h[b], rows[differ], r=r)
+            check_sets(gi[differ], gc[differ], o_idx[differ], o_cnt[differ], sc)
+        o = oracle.attend_rows(d["q"][b], d["k"][b], d["v"][b], rows, gi, gc, r=r)
+        err = rel_err(g_out[b][rows], o)
+        say("r=%d seq %d: %d rows, %d differ, attention rel err %.2e" % (r, b, len(rows),
+                                                                        len(differ), err))
+        assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("r,n_q,lens", [(1, 1, (9000, 4097, 2050)), (8, 4, (9000, 9001, 5003)),
+                                        (16, 1, (40000, 1999, 16391)),
+                                        (2, 4, (9002, 7000, 1027))])
+def test_block_size_variants_decode(r, n_q, lens):
+    say("block size decode r=%d n_q=%d lens=%s" % (r, n_q, lens))
+    lens = list(lens)
+    n = max(lens)
+    K = 2048
+    p = qsa.params(r=r, K=K)
+    d = inputs.small(B=3, n=n, hq=16, hkv=2, dtype="bf16", r=r, K=K, seed=300 + r)
+    t = _dev_inputs(d)
+    kbar = torch.empty((3, n // r, 128), dtype=torch.bfloat16, device="cuda")
+    qsa.qsa_pool_keys(p, t["k_idx"], kbar, 0, n // r)
+    seq_len = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    qi = torch.stack([t["q_idx"][b, L - n_q:L] for b, L in enumerate(lens)]).contiguous()
+    qq = torch.stack([t["q"][b, L - n_q:L] for b, L in enumerate(lens)]).contiguous()
+    idx, cnt = _index_gpu(p, qi, kbar, seq_len=seq_len)
+    ws = qsa.workspace(qsa.qsa_sparse_attn_decode_workspace(p, 3, n_q, 16, 2))
+    out = torch.empty_like(qq)
+    qsa.qsa_sparse_attn_decode(p, qq, t["k"], t["v"], seq_len, idx, cnt, out, ws)
+    # the same tokens sharing the first token's selection
+    first_len = torch.tensor([L - n_q + 1 for L in lens], dtype=torch.int32, device="cuda")
+    sidx, scnt = _index_gpu(p, qi[:, :1].contiguous(), kbar, seq_len=first_len)
+    sout = torch.empty_like(qq)
+    qsa.qsa_sparse_attn_decode_shared(p, qq, t["k"], t["v"], seq_len, sidx, scnt, sout, ws)
+    torch.cuda.synchronize()
+    kbar_h, g_idx, g_cnt, g_out = to_host(kbar), to_host(idx), to_host(cnt), to_host(out)
+    s_idx, s_cnt, s_out = to_host(sidx), to_host(scnt), to_host(sout)
+    for b, L in enumerate(lens):
+        pos = np.arange(L - n_q, L)
+        o_idx, o_cnt = oracle.index_at(d["q_idx"][b][pos], kbar_h[b], pos, r=r, K=K)
+        sc = oracle.score_at(d["q_idx"][b][pos], kbar_h[b], pos, r=r)
+        check_sets(g_idx[b], g_cnt[b], o_idx, o_cnt, sc)
+        o = oracle.attend_at(d["q"][b][pos], d["k"][b], d["v"][b], pos, g_idx[b], g_cnt[b], r=r)
+        assert rel_err(g_out[b], o) <= TOL["bf16"]
+        os_ = oracle.attend_shared(d["q"][b][pos], d["k"][b], d["v"][b], L - n_q, pos,
+                                   s_idx[b, 0], s_cnt[b, 0], r=r)
+        assert rel_err(s_out[b], os_) <= TOL["bf16"]
 
 
 def test_decode_step_graph_replays():

@@ -78,6 +78,40 @@ def test_pool_partial_rope_leaves_upper_dims_and_norms():
 # RoPE ([hub] partial RoPE on 64 of 128 dims)
 # --------------------------------------------------------------------------
 
+# RMS-normalised pooling ([glide] "Qwen Sparse Attention" toy: average-pool,
+# then RMSNorm)
+
+def test_pool_rmsnorm_closed_form_without_rope():
+    """rope_dims = 0, eps = 0: every pooled key is the block mean divided by
+    its root mean square, times the gain (float32 storage: one rounding)."""
+    rng = np.random.default_rng(21)
+    k = rng.standard_normal((64, 128)).astype(np.float32)
+    gamma = rng.uniform(0.5, 2.0, 128)
+    got = oracle.pool_rmsnorm(k, gamma, eps=0.0, r=4, rope_dims=0)
+    mean = k.astype(np.float64).reshape(16, 4, 128).mean(axis=1)
+    rms = np.sqrt((mean ** 2).mean(axis=1, keepdims=True))
+    np.testing.assert_array_equal(got, (mean / rms * gamma).astype(np.float32))
+
+
+def test_pool_rmsnorm_invariances():
+    """Scaling every key by c > 0 leaves the normalised keys unchanged
+    (eps = 0); with unit gain every pooled key has RMS 1 up to one float32
+    rounding (the rotation keeps the sum of squares); eps > 0 only shrinks
+    it; the unrotated dims equal those of the unrotated result."""
+    rng = np.random.default_rng(22)
+    k = (rng.standard_normal((64, 128)) * 0.1).astype(np.float32)
+    ones = np.ones(128)
+    a = oracle.pool_rmsnorm(k, ones, eps=0.0)
+    b = oracle.pool_rmsnorm((k * np.float32(8.0)).astype(np.float32), ones, eps=0.0)
+    np.testing.assert_allclose(a, b, rtol=3e-7, atol=0)
+    rms = np.sqrt((a.astype(np.float64) ** 2).mean(axis=1))
+    np.testing.assert_allclose(rms, 1.0, rtol=2e-7)
+    c = oracle.pool_rmsnorm(k, ones, eps=1e-2)
+    assert np.all(np.sqrt((c.astype(np.float64) ** 2).mean(axis=1)) < rms)
+    d0 = oracle.pool_rmsnorm(k, ones, eps=0.0, rope_dims=0)
+    np.testing.assert_array_equal(a[:, 64:], d0[:, 64:])
+
+
 def test_rope_position_zero_is_identity():
     x = np.random.default_rng(3).standard_normal((5, 128))
     np.testing.assert_array_equal(oracle.rope_rows(x, [0] * 5), x)

@@ -36,7 +36,8 @@ static int num_cus() {
 
 static qsa_status check_params(const qsa_params* p) {
   if (!p) return fail(QSA_ERR_NULL, "params is NULL");
-  if (p->r != 4) return fail(QSA_ERR_UNSUPPORTED, "r=%d: only r=4 is built", p->r);
+  if (p->r != 1 && p->r != 2 && p->r != 4 && p->r != 8 && p->r != 16)
+    return fail(QSA_ERR_UNSUPPORTED, "r=%d: built for r in {1, 2, 4, 8, 16}", p->r);
   if (p->K < p->r) return fail(QSA_ERR_SHAPE, "K=%d must be >= r=%d", p->K, p->r);
   if (p->h_idx != 4) return fail(QSA_ERR_UNSUPPORTED, "h_idx=%d: only 4 indexer heads", p->h_idx);
   if (p->d_idx != 128) return fail(QSA_ERR_UNSUPPORTED, "d_idx=%d: only 128", p->d_idx);
@@ -100,8 +101,30 @@ qsa_status qsa_pool_keys(const qsa_params* p, qsa_dtype dtype, const void* k_idx
     return fail(QSA_ERR_SHAPE, "block_end=%lld exceeds nb_cap=%lld", (long long)block_end,
                 (long long)nb_cap);
   return launched(launch_pool(dtype, *p, k_idx, n_cap, kbar, nb_cap, B, block_begin, block_end,
-                              (hipStream_t)stream),
+                              nullptr, 0.f, (hipStream_t)stream),
                   "pool_keys");
+}
+
+qsa_status qsa_pool_keys_rmsnorm(const qsa_params* p, qsa_dtype dtype, const void* k_idx,
+                                 int64_t n_cap, const float* gamma, float eps, void* kbar,
+                                 int64_t nb_cap, int32_t B, int64_t block_begin,
+                                 int64_t block_end, void* stream) {
+  qsa_status s = check_params(p);
+  if (s) return s;
+  if ((s = check_dtype(dtype))) return s;
+  if (!k_idx || !kbar || !gamma) return fail(QSA_ERR_NULL, "k_idx, gamma or kbar is NULL");
+  if (!(eps >= 0.f) || !isfinite(eps)) return fail(QSA_ERR_SHAPE, "eps must be finite and >= 0");
+  if (B < 0 || n_cap < 0 || nb_cap < 0 || block_begin < 0 || block_begin > block_end)
+    return fail(QSA_ERR_SHAPE, "bad sizes or block range");
+  if (block_end * (int64_t)p->r > n_cap)
+    return fail(QSA_ERR_SHAPE, "block_end*r=%lld exceeds n_cap=%lld",
+                (long long)(block_end * p->r), (long long)n_cap);
+  if (block_end > nb_cap)
+    return fail(QSA_ERR_SHAPE, "block_end=%lld exceeds nb_cap=%lld", (long long)block_end,
+                (long long)nb_cap);
+  return launched(launch_pool(dtype, *p, k_idx, n_cap, kbar, nb_cap, B, block_begin, block_end,
+                              gamma, eps, (hipStream_t)stream),
+                  "pool_keys_rmsnorm");
 }
 
 static bool decode_split_path(int32_t n_q) { return n_q <= 4; }

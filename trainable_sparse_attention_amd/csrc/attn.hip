@@ -4,9 +4,10 @@
 //
 // One 64-lane wave handles one (sequence, query row, KV head, split) and the
 // hq/hkv query heads that share the KV head (GQA).  The token set is walked
-// in chunks of 8 slots (a slot is one selected block of r = 4 keys, or the
-// tail); each chunk gathers 8 KB of K and 8 KB of V (1 KB contiguous per
-// block per head in the head-major caches).
+// in chunks of 32 keys: 32/r slots (a slot is one selected block of r keys,
+// or a tail slot); each chunk gathers 8 KB of K and 8 KB of V (r * 256 bytes
+// contiguous per block per head in the head-major caches).  r is 1, 2, 4, 8
+// or 16 (the micro-block sizes the pages sweep).
 //
 // bf16: S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 (16 keys x
 //   16 heads per tile, heads beyond hq/hkv are zero); V is staged through
@@ -27,7 +28,8 @@ namespace qsa {
 
 namespace {
 
-constexpr int kSlotsPerChunk = 8;
+constexpr int kChunkKeys = 32;   // keys per chunk: two 16-key MFMA tiles
+constexpr int kSlotsPerChunk = 8;  // at r = 4
 constexpr int kVRow = 128 + 8;  // LDS row of V in bf16 elements (16 B pad)
 constexpr int kIdWin = 576;     // slot ids staged in LDS at a time (whole chunks)
 
@@ -133,10 +135,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // WIN: the row's slots may exceed one LDS window of ids (refilled as the
-// scan advances); otherwise every slot id is staged once.
-template <bool WIN>
+// scan advances); otherwise every slot id is staged once.  RR: tokens per
+// block (r); a chunk holds SPC = 32 / RR slots.
+template <bool WIN, int RR>
 __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, float* part,
                                                        int resident) {
+  constexpr int SPC = kChunkKeys / RR;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_attn[];
   unsigned short* vbuf = (unsigned short*)smem_attn;      // [32 keys][128]
   int* ids = (int*)(smem_attn + 32 * 128 * 2);              // block of each slot
@@ -147,14 +151,14 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
   const Row R = row_ctx(a, b, t);
   int s0 = 0, s1 = R.nslots;
   if (nsplit > 1) {
-    s0 = split * kSlotsPerChunk;
-    s1 = min(R.nslots, s0 + kSlotsPerChunk);
+    s0 = split * SPC;
+    s1 = min(R.nslots, s0 + SPC);
   }
-  // Block ids of a window of kIdWin slots from `base` (the tail slot is block
-  // nb; slots past the set read block 0 and are masked).
+  // Block ids of a window of kIdWin slots from `base` (tail slot j is block
+  // nb + j; slots past the set read block 0 and are masked).
   int base = s0;
   // (at most the window, and no further than the chunk that holds slot s1 - 1)
-  const int fill_n = min(kIdWin, (s1 - s0 + kSlotsPerChunk - 1) / kSlotsPerChunk * kSlotsPerChunk);
+  const int fill_n = min(kIdWin, (s1 - s0 + SPC - 1) / SPC * SPC);
   auto fill_ids = [&](int b0) {
     for (int u = lane; u < fill_n; u += 64) {
       const int sl = b0 + u;
@@ -166,8 +170,8 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
   // Token row of key tok of slot u with block id `id`, 0 if the key is not
   // in T_i (branch-free).
   auto row_sel = [&](int u, int id, int tok) -> uint32_t {
-    const bool ok = u < s1 && tok < slot_tokens(R, u, a.r);
-    return ok ? (uint32_t)id * (uint32_t)a.r + (uint32_t)tok : 0u;
+    const bool ok = u < s1 && tok < slot_tokens(R, u, RR);
+    return ok ? (uint32_t)id * (uint32_t)RR + (uint32_t)tok : 0u;
   };
   const int G = a.hq / a.hkv;
   const int head = g * G + hl;
@@ -186,38 +190,54 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
       qf[cc] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  // The 8 block ids of the chunk at slot s (every slot of a loaded chunk
-  // lies in the window).  Read as two broadcast 16-byte LDS loads and kept
-  // in registers, so the address math needs no further LDS round trips.
+  // The block ids of the chunk at slot s (every slot of a loaded chunk lies
+  // in the window), read as broadcast LDS loads and kept in registers, so
+  // the address math needs no further LDS round trips (r >= 4: one id per
+  // V instruction; below, each lane group reads its own slot's id).
+  constexpr int NID = SPC < 8 ? SPC : 8;
   auto chunk_ids = [&](int s, int* id) {
-    const int4* p = (const int4*)(ids + (s - base));
-    const int4 x = p[0], y = p[1];
-    id[0] = x.x; id[1] = x.y; id[2] = x.z; id[3] = x.w;
-    id[4] = y.x; id[5] = y.y; id[6] = y.z; id[7] = y.w;
+    if constexpr (NID >= 4) {
+      const int4* p = (const int4*)(ids + (s - base));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(id[i]));
+      for (int j = 0; j < NID / 4; ++j) {
+        const int4 x = p[j];
+        id[4 * j] = x.x; id[4 * j + 1] = x.y; id[4 * j + 2] = x.z; id[4 * j + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NID; ++j) id[j] = ids[s - base + j];
+    }
+#pragma unroll
+    for (int i = 0; i < NID; ++i) asm volatile("" : "+v"(id[i]));
   };
-  // K operands of a chunk: key row hl of tile kt = slot s + 4kt + hl/4,
-  // token hl%4, dims 32cc + 8gq.
+  // K operands of a chunk: key row hl of tile kt = key 16kt + hl of the
+  // chunk = slot s + (16kt + hl) / RR, token (16kt + hl) % RR; dims 32cc + 8gq.
   auto load_k = [&](int s, bf16x8 (*kf)[4]) {
-    const int q = hl >> 2;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      int bid = ids[s - base + 4 * kt + q];
+      const int key = 16 * kt + hl;
+      int bid = ids[s - base + key / RR];
       asm volatile("" : "+v"(bid));
-      const uint32_t off = row_sel(s + 4 * kt + q, bid, hl & 3) * 256u + 16u * gq;
+      const uint32_t off = row_sel(s + key / RR, bid, key % RR) * 256u + 16u * gq;
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) kf[kt][cc] = *(const bf16x8*)(kb + off + 64 * cc);
     }
   };
-  // V of a chunk straight into LDS: instruction i moves slot s + i (1 KB);
-  // lane l's 16 bytes land at key 4i + l/16, chunk position l%16 of that key
-  // row, so the lane fetches the logical chunk stored there.
+  // V of a chunk straight into LDS: instruction i moves keys 4i .. 4i + 3
+  // (1 KB); lane l's 16 bytes land at key 4i + l/16, chunk position l%16 of
+  // that key row, so the lane fetches the logical chunk stored there.
   auto load_v = [&](int s, const int* id, unsigned short* dst) {
 #pragma unroll
-    for (int i = 0; i < kSlotsPerChunk; ++i) {
+    for (int i = 0; i < 8; ++i) {
       const int kk = 4 * i + (lane >> 4);
-      const uint32_t off = row_sel(s + i, id[i], lane >> 4) * 256u + 16u * vswz(kk, lane & 15);
+      int bid;
+      if constexpr (RR >= 4) {
+        bid = id[4 * i / RR];
+      } else {
+        bid = ids[s - base + kk / RR];
+      }
+      const uint32_t off =
+          row_sel(s + kk / RR, bid, kk % RR) * 256u + 16u * vswz(kk, lane & 15);
       __builtin_amdgcn_global_load_lds((glb_void_t*)(vb + off), (lds_void_t*)(dst + i * 512), 16,
                                        0, 0);
     }
@@ -239,21 +259,21 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
   // on the launch index, so a chunked prefill sums in the same order.
   // A wave loads one chunk (K to registers, V to LDS) and computes it; the
   // latency is hidden by the other resident waves.
-  const int nch = (s1 - s0 + kSlotsPerChunk - 1) / kSlotsPerChunk;
+  const int nch = (s1 - s0 + SPC - 1) / SPC;
   int ph = 0;
   if (!WIN && nsplit == 1 && resident > 0 && nch > 0)
     ph = (int)(((R.pos * a.hkv + g) * nch / resident) % nch);
   for (int cc = 0; cc < nch; ++cc) {
     int c = ph + cc;
     if (c >= nch) c -= nch;
-    const int s = s0 + kSlotsPerChunk * c;
+    const int s = s0 + SPC * c;
     if constexpr (WIN) {
-      if (s + kSlotsPerChunk - base > kIdWin) {
+      if (s + SPC - base > kIdWin) {
         base = s;
         fill_ids(base);
       }
     }
-    int id[8];
+    int id[NID];
     chunk_ids(s, id);
     bf16x8 kc[2][4];
     load_k(s, kc);
@@ -268,15 +288,17 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
         sacc[kt] =
             __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc[kt][cc], qf[cc], sacc[kt], 0, 0, 0);
     }
+    // key 16kt + 4gq + i of the chunk: slot s + key / RR, token key % RR
     float sv[8];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const int u = s + 4 * kt + gq;
-      const bool slot_ok = u < s1;
-      const int ntok = slot_ok ? slot_tokens(R, u, a.r) : 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sv[4 * kt + i] = (slot_ok && i < ntok) ? sacc[kt][i] * sl2 : -INFINITY;
+      for (int i = 0; i < 4; ++i) {
+        const int key = 16 * kt + 4 * gq + i;
+        const int u = s + key / RR;
+        const bool ok = u < s1 && key % RR < slot_tokens(R, u, RR);
+        sv[4 * kt + i] = ok ? sacc[kt][i] * sl2 : -INFINITY;
+      }
     }
     float mx = sv[0];
 #pragma unroll
@@ -380,10 +402,12 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, int nsplit, fl
   int b, t, g, split;
   decode_job(a, nsplit, &b, &t, &g, &split);
   const Row R = row_ctx(a, b, t);
+  // key k of a chunk at slot s: slot s + k / r, token k % r
+  const int r = a.r, spc = kChunkKeys / r;
   int s0 = 0, s1 = R.nslots;
   if (nsplit > 1) {
-    s0 = split * kSlotsPerChunk;
-    s1 = min(R.nslots, s0 + kSlotsPerChunk);
+    s0 = split * spc;
+    s1 = min(R.nslots, s0 + spc);
   }
   const int G = a.hq / a.hkv;
   const int head = g * G + hl;
@@ -410,12 +434,13 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, int nsplit, fl
   for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
 
-  for (int s = s0; s < s1; s += kSlotsPerChunk) {
+  for (int s = s0; s < s1; s += spc) {
     f32x4 sacc[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       int64_t row;
-      slot_row(R, s + 4 * kt + (hl >> 2), s1, hl & 3, a.r, &row);
+      const int key = 16 * kt + hl;
+      slot_row(R, s + key / r, s1, key % r, r, &row);
       const float* kr = ks + row * 128 + 32 * gq;
       sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -429,11 +454,11 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, int nsplit, fl
     float sv[8];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const int u = s + 4 * kt + gq;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         int64_t row;
-        const bool ok = slot_row(R, u, s1, i, a.r, &row);
+        const int key = 16 * kt + 4 * gq + i;
+        const bool ok = slot_row(R, s + key / r, s1, key % r, r, &row);
         sv[4 * kt + i] = ok ? sacc[kt][i] * sl2 : -INFINITY;
       }
     }
@@ -460,7 +485,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, int nsplit, fl
     for (int cc = 0; cc < 8; ++cc) {
       const int key = (cc < 4) ? (4 * gq + cc) : (16 + 4 * gq + cc - 4);
       int64_t row;
-      slot_row(R, s + (key >> 2), s1, key & 3, a.r, &row);
+      slot_row(R, s + key / r, s1, key % r, r, &row);
       const float* vr = vsrc + row * 128 + 8 * hl;
       const f32x4 v0 = *(const f32x4*)vr;
       const f32x4 v1 = *(const f32x4*)(vr + 4);
@@ -623,7 +648,7 @@ static int resident_waves() {
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (dev == dev_cached) return res_cached;
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_bf16_kernel<false>, 64,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_bf16_kernel<false, 4>, 64,
                                                    bf16_lds_prefill()) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
@@ -638,8 +663,36 @@ static int max_tail_slots(int r, int n_q, bool shared) {
   const int tail = r - 1 + (shared ? n_q - 1 : 0);
   return (tail + r - 1) / r;
 }
+// A split of the decode attention is one chunk: 32 / r slots.
 static int decode_splits(int kB, int r, int n_q, bool shared) {
-  return (kB + max_tail_slots(r, n_q, shared) + kSlotsPerChunk - 1) / kSlotsPerChunk;
+  const int spc = kChunkKeys / r;
+  return (kB + max_tail_slots(r, n_q, shared) + spc - 1) / spc;
+}
+
+template <bool WIN>
+static void launch_bf16(const AttnArgs& a, dim3 grid, size_t lds, hipStream_t st, int nsplit,
+                        float* part, int resident) {
+  switch (a.r) {
+    case 1:
+      hipLaunchKernelGGL((attn_bf16_kernel<WIN, 1>), grid, dim3(64), lds, st, a, nsplit, part,
+                         resident);
+      break;
+    case 2:
+      hipLaunchKernelGGL((attn_bf16_kernel<WIN, 2>), grid, dim3(64), lds, st, a, nsplit, part,
+                         resident);
+      break;
+    case 8:
+      hipLaunchKernelGGL((attn_bf16_kernel<WIN, 8>), grid, dim3(64), lds, st, a, nsplit, part,
+                         resident);
+      break;
+    case 16:
+      hipLaunchKernelGGL((attn_bf16_kernel<WIN, 16>), grid, dim3(64), lds, st, a, nsplit, part,
+                         resident);
+      break;
+    default:
+      hipLaunchKernelGGL((attn_bf16_kernel<WIN, 4>), grid, dim3(64), lds, st, a, nsplit, part,
+                         resident);
+  }
 }
 
 hipError_t launch_attn_prefill(qsa_dtype dt, const AttnArgs& a, hipStream_t st) {
@@ -647,12 +700,12 @@ hipError_t launch_attn_prefill(qsa_dtype dt, const AttnArgs& a, hipStream_t st) 
   if (waves == 0) return hipSuccess;
   if (dt == QSA_BF16) {
     // every slot id fits one window
-    if (a.kB + max_tail_slots(a.r, a.n_q, a.shared) + kSlotsPerChunk <= kIdWin)
-      hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3((unsigned)waves), dim3(64),
-                         bf16_lds_prefill(), st, a, 1, (float*)nullptr, resident_waves());
+    const int spc = kChunkKeys / a.r;
+    if (a.kB + max_tail_slots(a.r, a.n_q, a.shared) + spc <= kIdWin)
+      launch_bf16<false>(a, dim3((unsigned)waves), bf16_lds_prefill(), st, 1, nullptr,
+                         resident_waves());
     else
-      hipLaunchKernelGGL(attn_bf16_kernel<true>, dim3((unsigned)waves), dim3(64),
-                         bf16_lds_prefill(), st, a, 1, (float*)nullptr, 0);
+      launch_bf16<true>(a, dim3((unsigned)waves), bf16_lds_prefill(), st, 1, nullptr, 0);
   }
   else
     hipLaunchKernelGGL(attn_f32_kernel, dim3((unsigned)waves), dim3(64), 0, st, a, 1,
@@ -699,8 +752,7 @@ hipError_t launch_attn_decode(qsa_dtype dt, const AttnArgs& a, void* ws, hipStre
   if (waves == 0) return hipSuccess;
   float* part = (float*)ws;
   if (dt == QSA_BF16)
-    hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3((unsigned)waves), dim3(64), bf16_lds_need(),
-                       st, a, nsplit, part, 0);
+    launch_bf16<false>(a, dim3((unsigned)waves), bf16_lds_need(), st, nsplit, part, 0);
   else
     hipLaunchKernelGGL(attn_f32_kernel, dim3((unsigned)waves), dim3(64), 0, st, a, nsplit, part);
   hipError_t e = hipGetLastError();

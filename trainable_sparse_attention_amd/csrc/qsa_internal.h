@@ -69,9 +69,10 @@ constexpr int64_t kMaxCapBf16 = (int64_t)1 << 24;
 
 // ---- host launchers (defined in the kernel translation units) ------------
 
+// gamma == nullptr: plain block mean; else RMS-normalised mean * gamma
 hipError_t launch_pool(qsa_dtype dt, const qsa_params& p, const void* k_idx, int64_t n_cap,
                        void* kbar, int64_t nb_cap, int B, int64_t b0, int64_t b1,
-                       hipStream_t st);
+                       const float* gamma, float eps, hipStream_t st);
 
 struct IndexArgs {
   const void* q_idx;

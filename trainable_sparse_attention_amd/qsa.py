@@ -18,7 +18,8 @@ STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL", 2: "QSA_ERR_SHAPE", 3: "QSA_ERR_DTYPE"
 
 # every symbol the headers in include/ declare
 EXPORTS = ["qsa_default_params", "qsa_k_blocks", "qsa_status_str", "qsa_last_error",
-           "qsa_pool_keys", "qsa_index_topk", "qsa_index_topk_workspace",
+           "qsa_pool_keys", "qsa_pool_keys_rmsnorm", "qsa_index_topk",
+           "qsa_index_topk_workspace",
            "qsa_sparse_attn_prefill", "qsa_sparse_attn_decode",
            "qsa_sparse_attn_decode_workspace", "qsa_sparse_attn_decode_shared",
            "qsa_sparse_attn_decode_noalloc",
@@ -61,6 +62,9 @@ def lib():
         L.qsa_last_error.restype = ctypes.c_char_p
         L.qsa_pool_keys.argtypes = [PP, ctypes.c_int, P, I64, P, I64, I32, I64, I64, P]
         L.qsa_pool_keys.restype = ctypes.c_int
+        L.qsa_pool_keys_rmsnorm.argtypes = [PP, ctypes.c_int, P, I64, P, F, P, I64, I32, I64, I64,
+                                            P]
+        L.qsa_pool_keys_rmsnorm.restype = ctypes.c_int
         L.qsa_index_topk.argtypes = [PP, ctypes.c_int, P, P, I64, I32, I32, I64, P, P, P, P, SZ,
                                      P]
         L.qsa_index_topk.restype = ctypes.c_int
@@ -128,6 +132,15 @@ def qsa_pool_keys(p, k_idx, kbar, block_begin, block_end, stream=None):
     _check(lib().qsa_pool_keys(ctypes.byref(p), dtype_code(k_idx), _ptr(k_idx), n_cap,
                                _ptr(kbar), kbar.shape[1], B, block_begin, block_end,
                                _stream(stream)))
+
+
+def qsa_pool_keys_rmsnorm(p, k_idx, gamma, eps, kbar, block_begin, block_end, stream=None):
+    """As qsa_pool_keys with the block mean RMS-normalised (gain gamma, a
+    float32 [128] device tensor) before the rotation."""
+    B, n_cap, _ = k_idx.shape
+    _check(lib().qsa_pool_keys_rmsnorm(ctypes.byref(p), dtype_code(k_idx), _ptr(k_idx), n_cap,
+                                       _ptr(gamma), eps, _ptr(kbar), kbar.shape[1], B,
+                                       block_begin, block_end, _stream(stream)))
 
 
 def qsa_index_topk_workspace(p, dtype, B, n_q, nb_cap, decode):
