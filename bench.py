@@ -53,6 +53,8 @@ def parse():
                     help="comma-separated further decode workloads ('' for none)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense GQA comparison (chunked prefill and decode)")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=16384,
                     help="uniformly spaced prefill rows the CPU oracle computes")
@@ -334,6 +336,83 @@ def bench_decode(name, args, torch, qsa, inputs, flush, shared=False):
                 index_gbs=scan_bytes / (st[1] * 1e-3) / 1e9)
 
 
+def bench_dense_comparison(args, torch, qsa, inputs, flush):
+    """The pages' kernel comparison ([glide] "QSA Ablations and Efficiency",
+    Figure 6(c,d)): (c) chunked prefill, one 16K-token chunk at the end of a
+    context of L tokens, batch 1: QSA (pool the chunk's blocks, index + top-k
+    for the chunk's rows, sparse attention) against dense causal GQA
+    attention of the same rows; (d) decode at batch 4 with 4 new tokens per
+    sequence at 1M: the QSA step against dense attention of the 4 tokens."""
+    d = inputs.make("prefill_1m", seed=6, backend="torch")
+    p = qsa.params()
+    n, hq, hkv = d["n"], d["hq"], d["hkv"]
+    kB = qsa.k_blocks(p)
+    dev = d["q"].device
+    stream = torch.cuda.current_stream()
+    kbar = torch.empty((1, n // p.r, 128), dtype=torch.bfloat16, device=dev)
+    qsa.qsa_pool_keys(p, d["k_idx"], kbar, 0, n // p.r)
+    C = 16384
+    ws = qsa.workspace(qsa.qsa_index_topk_workspace(p, qsa.QSA_BF16, 1, C, n // p.r, False))
+    idx = torch.empty((1, C, kB), dtype=torch.int32, device=dev)
+    cnt = torch.empty((1, C), dtype=torch.int32, device=dev)
+    out = torch.empty((1, C, hq, 128), dtype=torch.bfloat16, device=dev)
+    out_d = torch.empty_like(out)
+    rows = []
+    for L in [131072, 262144, 524288, 1048576]:
+        p0 = L - C
+        qi = d["q_idx"][:, p0:L]
+        qq = d["q"][:, p0:L]
+        stages = [lambda: qsa.qsa_pool_keys(p, d["k_idx"], kbar, p0 // p.r, L // p.r, stream),
+                  lambda: qsa.qsa_index_topk(p, qi, kbar, idx, cnt, ws, p0, None, stream),
+                  lambda: qsa.qsa_sparse_attn_prefill(p, qq, d["k"], d["v"], idx, cnt, out, p0,
+                                                      0.0, stream)]
+        dense = [lambda: qsa.qsa_dense_attn_prefill(qq, d["k"], d["v"], out_d, p0, 0.0, stream)]
+        for f in stages + dense:
+            f()
+        ms_q, st_q = time_steps(torch, stream, stages, 3, flush)
+        ms_d, _ = time_steps(torch, stream, dense, 2, flush)
+        flop_d = 4.0 * 128 * hq * (C * p0 + C * (C + 1) / 2)
+        rows.append({"context": L, "chunk": C, "qsa_ms": ms_q,
+                     "qsa_stage_ms": {"pool_keys": st_q[0], "index_topk": st_q[1],
+                                      "sparse_attn_prefill": st_q[2]},
+                     "dense_ms": ms_d, "dense_TFLOP/s": flop_d / (ms_d * 1e-3) / 1e12,
+                     "dense_frac_mfma": flop_d / (ms_d * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                     "speedup": ms_d / ms_q})
+        log("chunked prefill, 16K chunk at %d: QSA %.3f ms (pool %.3f, index %.3f, attn %.3f), "
+            "dense %.3f ms (%.0f TFLOP/s): %.2fx" % (L, ms_q, *st_q, ms_d,
+                                                    flop_d / (ms_d * 1e-3) / 1e12, ms_d / ms_q))
+    del d, kbar, ws, idx, cnt, out, out_d
+    torch.cuda.empty_cache()
+    # decode, batch 4, 4 new tokens per sequence, 1M context: dense attention
+    dd = inputs.make("decode_4x1m_next4", seed=4, backend="torch")
+    B, L, n_q = dd["B"], dd["n"], dd["n_q"]
+    seq_len = torch.full((B,), L, dtype=torch.int32, device=dev)
+    out = torch.empty_like(dd["q"])
+    ws = qsa.workspace(qsa.qsa_dense_attn_decode_workspace(B, n_q, hkv, L))
+    step = [lambda: qsa.qsa_dense_attn_decode(dd["q"], dd["k"], dd["v"], seq_len, out, ws)]
+    for f in step:
+        f()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step[0]()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        step[0]()
+    gr.replay()
+    ms_dd, _ = time_steps(torch, stream, [gr.replay], args.decode_steps, flush)
+    kv_bytes = B * hkv * L * 128 * 2 * 2
+    log("dense decode, batch 4 x 4 new tokens at 1M: %.4f ms (%.0f GB/s of K/V)" % (
+        ms_dd, kv_bytes / (ms_dd * 1e-3) / 1e9))
+    return {"chunked_prefill": rows,
+            "decode_b4_next4_1m": {"dense_ms": ms_dd,
+                                   "dense_GB/s": kv_bytes / (ms_dd * 1e-3) / 1e9,
+                                   "dense_frac_hbm": kv_bytes / (ms_dd * 1e-3) / 1e9 /
+                                   PEAK_HBM_GBS}}
+
+
 def decode_record(inputs, dec, steps):
     return {
         "value": dec["tok_s"], "unit": "tokens/s", "ms_per_step": dec["ms"],
@@ -433,6 +512,16 @@ def main():
             decs.append(dec)
             torch.cuda.empty_cache()
 
+    cmp_ = None
+    if not args.no_dense:
+        cmp_ = bench_dense_comparison(args, torch, qsa, inputs, flush)
+        qsa_dec = {x["name"]: x["ms"] for x in decs}
+        if "decode_4x1m_next4_shared" in qsa_dec:
+            dm = cmp_["decode_b4_next4_1m"]
+            for name in ("decode_4x1m_next4", "decode_4x1m_next4_shared"):
+                dm[name + "_ms"] = qsa_dec[name]
+                dm["speedup_" + name] = dm["dense_ms"] / qsa_dec[name]
+
     st = pre["stage_ms"]
     attn_ms = st[2]
     attn_tflops = pre["attn_flop"] / (attn_ms * 1e-3) / 1e12
@@ -490,6 +579,8 @@ def main():
                                     "sum_T": pre["slots"], "gather": gather},
         },
     }
+    if cmp_ is not None:
+        line["qsa_vs_dense"] = cmp_
     if decs:
         line["decode"] = decode_record(inputs, decs[0], args.decode_steps)
         if len(decs) > 1:

@@ -258,6 +258,44 @@ qsa_status qsa_sparse_attn_decode_noalloc(const qsa_params* p, qsa_dtype dtype, 
                                           int32_t n_q, int32_t hq, int32_t hkv, int32_t d,
                                           float scale, void* out, void* stream);
 
+/*
+ * qsa_dense_attn_prefill -- dense causal GQA attention: every query attends
+ * to all tokens 0 .. its position.  This is QSA with every block selected
+ * (k_B at least the visible blocks), and the dense baseline of the pages'
+ * kernel comparison ([glide] "QSA Ablations and Efficiency", Figure 6(c):
+ * chunked prefill, 16K-token chunks, batch 1, dense GQA vs QSA).
+ *
+ *   out[b][t][h] = sum_{j <= q_pos0 + t} softmax_j(scale <q[b][t][h], k[b][g][j]>) v[b][g][j]
+ *   q : [B][n_q][hq][d] (rows at positions q_pos0 + t); k, v : [B][hkv][n_cap][d]
+ *   out : [B][n_q][hq][d]; bfloat16 only; hq / hkv must divide 16; scale <= 0
+ *   means 1/sqrt(d).
+ * Errors: NULL pointers; q_pos0 + n_q > n_cap -> QSA_ERR_SHAPE; float32,
+ * d != 128 or hq/hkv not dividing 16 -> QSA_ERR_UNSUPPORTED.
+ */
+qsa_status qsa_dense_attn_prefill(qsa_dtype dtype, const void* q, const void* k, const void* v,
+                                  int64_t n_cap, int32_t B, int32_t n_q, int64_t q_pos0,
+                                  int32_t hq, int32_t hkv, int32_t d, float scale, void* out,
+                                  void* stream);
+
+/*
+ * qsa_dense_attn_decode -- the same for n_q new tokens per sequence at
+ * positions d_seq_len[b] - n_q + t against the KV caches ([glide] Figure
+ * 6(d): decode, batch 4, next_n = 4), split over the context in pieces of
+ * 4096 keys and combined.
+ *   q : [B][n_q][hq][d]; caches [B][hkv][n_cap][d]; d_seq_len device int32
+ *   [B] (includes the new tokens, <= n_cap); out : [B][n_q][hq][d];
+ *   workspace : qsa_dense_attn_decode_workspace(B, n_q, hkv, n_cap) bytes.
+ * Errors as for qsa_dense_attn_prefill, plus n_q * hq/hkv > 64 ->
+ * QSA_ERR_UNSUPPORTED and a small workspace -> QSA_ERR_WORKSPACE.
+ */
+qsa_status qsa_dense_attn_decode(qsa_dtype dtype, const void* q, const void* k_cache,
+                                 const void* v_cache, int64_t n_cap, const int32_t* d_seq_len,
+                                 int32_t B, int32_t n_q, int32_t hq, int32_t hkv, int32_t d,
+                                 float scale, void* out, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+size_t qsa_dense_attn_decode_workspace(int32_t B, int32_t n_q, int32_t hkv, int64_t n_cap);
+
 #ifdef __cplusplus
 }
 #endif

@@ -461,6 +461,65 @@ def test_block_size_variants_decode(r, n_q, lens):
         assert rel_err(s_out[b], os_) <= TOL["bf16"]
 
 
+# ---- dense causal GQA attention (QSA with every block selected; the
+# pages' dense baseline, [glide] "QSA Ablations and Efficiency", Figure 6) ----
+
+def _dense_ref(q_rows, k, v, pos):
+    """The oracle's attention with every complete block selected: T = 0..pos."""
+    pos = np.asarray(pos, dtype=np.int64)
+    nbmax = int((pos.max() + 1) // 4)
+    idx = np.full((pos.size, max(nbmax, 1)), -1, dtype=np.int32)
+    cnt = ((pos + 1) // 4).astype(np.int32)
+    for u, c in enumerate(cnt):
+        idx[u, :c] = np.arange(c)
+    return oracle.attend_at(q_rows, k, v, pos, idx, cnt)
+
+
+@pytest.mark.parametrize("n,q_pos0,n_q,hq,hkv", [(3000, 0, 3000, 16, 2), (20000, 12000, 5001, 16, 2),
+                                                 (1003, 0, 1003, 8, 2), (4500, 100, 4400, 16, 1),
+                                                 (700, 650, 50, 2, 2)])
+def test_dense_prefill(n, q_pos0, n_q, hq, hkv):
+    say("dense prefill n=%d q_pos0=%d n_q=%d hq=%d hkv=%d" % (n, q_pos0, n_q, hq, hkv))
+    d = inputs.small(B=2, n=n, hq=hq, hkv=hkv, dtype="bf16", seed=400 + n_q)
+    t = _dev_inputs(d)
+    q = t["q"][:, q_pos0:q_pos0 + n_q].contiguous()
+    out = torch.empty_like(q)
+    qsa.qsa_dense_attn_prefill(q, t["k"], t["v"], out, q_pos0)
+    torch.cuda.synchronize()
+    g = to_host(out)
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([np.arange(min(8, n_q)), rng.integers(0, n_q, 96),
+                                     np.arange(max(0, n_q - 8), n_q)]))
+    for b in range(2):
+        o = _dense_ref(d["q"][b][q_pos0 + rows], d["k"][b], d["v"][b], q_pos0 + rows)
+        err = rel_err(g[b][rows], o)
+        say("dense prefill seq %d: %d rows, rel err %.2e" % (b, rows.size, err))
+        assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("n_q,lens,hq,hkv", [(1, (9000, 4097, 100), 16, 2),
+                                             (4, (9000, 9001, 5003), 16, 2),
+                                             (4, (300, 8191, 4096), 8, 2),
+                                             (6, (5000, 2000, 6001), 16, 2)])
+def test_dense_decode(n_q, lens, hq, hkv):
+    say("dense decode n_q=%d lens=%s" % (n_q, lens))
+    lens = list(lens)
+    n = max(lens)
+    d = inputs.small(B=3, n=n, hq=hq, hkv=hkv, dtype="bf16", seed=500 + n_q)
+    t = _dev_inputs(d)
+    seq_len = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    qq = torch.stack([t["q"][b, L - n_q:L] for b, L in enumerate(lens)]).contiguous()
+    out = torch.empty_like(qq)
+    ws = qsa.workspace(qsa.qsa_dense_attn_decode_workspace(3, n_q, hkv, n))
+    qsa.qsa_dense_attn_decode(qq, t["k"], t["v"], seq_len, out, ws)
+    torch.cuda.synchronize()
+    g = to_host(out)
+    for b, L in enumerate(lens):
+        pos = np.arange(L - n_q, L)
+        o = _dense_ref(d["q"][b][pos], d["k"][b], d["v"][b], pos)
+        assert rel_err(g[b], o) <= TOL["bf16"]
+
+
 def test_decode_step_graph_replays():
     """A decode step (pool the newest block, index, attend) captured in a HIP
     graph: every replay, with eager work and synchronizations between the

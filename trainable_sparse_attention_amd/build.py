@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libqsa.so")
 SOURCES = ["abi.hip", "pool_keys.hip", "index_prefill.hip", "index_exact.hip", "index_decode.hip",
-           "attn.hip", "probe_gather.hip"]
+           "attn.hip", "dense_attn.hip", "probe_gather.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Wno-unused-function", "-Wno-unused-variable",

@@ -364,6 +364,81 @@ qsa_status qsa_sparse_attn_decode_noalloc(const qsa_params* p, qsa_dtype dtype, 
                   "sparse_attn_decode_noalloc");
 }
 
+static qsa_status check_dense(qsa_dtype dtype, const void* q, const void* k, const void* v,
+                              void* out, int32_t B, int32_t n_q, int32_t hq, int32_t hkv,
+                              int32_t d, int64_t n_cap) {
+  qsa_status s = check_dtype(dtype);
+  if (s) return s;
+  if (dtype != QSA_BF16) return fail(QSA_ERR_UNSUPPORTED, "dense attention is built for bf16");
+  if (!q || !k || !v || !out) return fail(QSA_ERR_NULL, "NULL tensor argument");
+  if (B < 0 || n_q < 1 || hq < 1 || hkv < 1 || n_cap < 1)
+    return fail(QSA_ERR_SHAPE, "B>=0, n_q>=1, hq>=1, hkv>=1, n_cap>=1");
+  if (hq % hkv) return fail(QSA_ERR_SHAPE, "hq=%d not a multiple of hkv=%d", hq, hkv);
+  if (16 % (hq / hkv))
+    return fail(QSA_ERR_UNSUPPORTED, "hq/hkv=%d must divide 16", hq / hkv);
+  if (d != 128) return fail(QSA_ERR_UNSUPPORTED, "head dim %d: only 128", d);
+  return QSA_OK;
+}
+
+qsa_status qsa_dense_attn_prefill(qsa_dtype dtype, const void* q, const void* k, const void* v,
+                                  int64_t n_cap, int32_t B, int32_t n_q, int64_t q_pos0,
+                                  int32_t hq, int32_t hkv, int32_t d, float scale, void* out,
+                                  void* stream) {
+  qsa_status s = check_dense(dtype, q, k, v, out, B, n_q, hq, hkv, d, n_cap);
+  if (s) return s;
+  if (q_pos0 < 0 || q_pos0 + n_q > n_cap)
+    return fail(QSA_ERR_SHAPE, "positions [%lld, %lld) exceed n_cap=%lld", (long long)q_pos0,
+                (long long)(q_pos0 + n_q), (long long)n_cap);
+  if (B == 0) return QSA_OK;
+  AttnArgs a = {};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.n_cap = n_cap;
+  a.q_pos0 = q_pos0;
+  a.B = B;
+  a.n_q = n_q;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.scale = scale > 0.f ? scale : 1.f / sqrtf((float)d);
+  return launched(launch_dense_prefill(a, (hipStream_t)stream), "dense_attn_prefill");
+}
+
+size_t qsa_dense_attn_decode_workspace(int32_t B, int32_t n_q, int32_t hkv, int64_t n_cap) {
+  if (B <= 0 || n_q <= 0 || hkv <= 0 || n_cap <= 0) return 0;
+  return dense_decode_workspace(B, n_q, hkv, n_cap);
+}
+
+qsa_status qsa_dense_attn_decode(qsa_dtype dtype, const void* q, const void* k_cache,
+                                 const void* v_cache, int64_t n_cap, const int32_t* d_seq_len,
+                                 int32_t B, int32_t n_q, int32_t hq, int32_t hkv, int32_t d,
+                                 float scale, void* out, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  qsa_status s = check_dense(dtype, q, k_cache, v_cache, out, B, n_q, hq, hkv, d, n_cap);
+  if (s) return s;
+  if (!d_seq_len) return fail(QSA_ERR_NULL, "d_seq_len is NULL");
+  if (n_q * (hq / hkv) > 64)
+    return fail(QSA_ERR_UNSUPPORTED, "n_q * hq/hkv = %d > 64", n_q * (hq / hkv));
+  if (B == 0) return QSA_OK;
+  const size_t need = dense_decode_workspace(B, n_q, hkv, n_cap);
+  if (!workspace || workspace_bytes < need)
+    return fail(QSA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  AttnArgs a = {};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.out = out;
+  a.seq_len = d_seq_len;
+  a.n_cap = n_cap;
+  a.B = B;
+  a.n_q = n_q;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.scale = scale > 0.f ? scale : 1.f / sqrtf((float)d);
+  return launched(launch_dense_decode(a, workspace, (hipStream_t)stream), "dense_attn_decode");
+}
+
 qsa_status qsa_probe_gather(const qsa_params* p, const void* k, const void* v, int64_t n_cap,
                             const int32_t* idx, const int32_t* cnt, int32_t B, int32_t n_q,
                             int64_t q_pos0, int32_t hkv, int32_t waves_per_cu, int32_t depth,

@@ -107,8 +107,6 @@ __device__ __forceinline__ void decode_job(const AttnArgs& a, int nsplit, int* b
 
 }  // namespace
 
-// part layout per (b, t, g, split): m[16], l[16], o[16][128] floats.
-constexpr int kPartFloats = 16 + 16 + 16 * 128;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
@@ -757,13 +755,18 @@ hipError_t launch_attn_decode(qsa_dtype dt, const AttnArgs& a, void* ws, hipStre
     hipLaunchKernelGGL(attn_f32_kernel, dim3((unsigned)waves), dim3(64), 0, st, a, nsplit, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_attn_combine(dt, a, nsplit, part, st);
+}
+
+hipError_t launch_attn_combine(qsa_dtype dt, const AttnArgs& a, int nsplit, const float* part,
+                               hipStream_t st) {
   const dim3 cg((unsigned)((int64_t)a.B * a.n_q * a.hq));
   if (dt == QSA_BF16)
     hipLaunchKernelGGL(attn_combine_kernel<unsigned short>, cg, dim3(128 * kCombGroups),
-                       nsplit * sizeof(float), st, a, nsplit, (const float*)part);
+                       nsplit * sizeof(float), st, a, nsplit, part);
   else
     hipLaunchKernelGGL(attn_combine_kernel<float>, cg, dim3(128 * kCombGroups),
-                       nsplit * sizeof(float), st, a, nsplit, (const float*)part);
+                       nsplit * sizeof(float), st, a, nsplit, part);
   return hipGetLastError();
 }
 

@@ -115,7 +115,19 @@ struct AttnArgs {
   float scale;
 };
 
+// split partial per (sequence, token, KV head, split): m[16], l[16],
+// o[16][128] floats (16 query heads per KV head at most); m in log2 units,
+// o and l relative to 2^m
+constexpr int kPartFloats = 16 + 16 + 16 * 128;
+
 hipError_t launch_attn_prefill(qsa_dtype dt, const AttnArgs& a, hipStream_t st);
+// merge nsplit partials per (sequence, token, KV head) into a.out
+hipError_t launch_attn_combine(qsa_dtype dt, const AttnArgs& a, int nsplit, const float* part,
+                               hipStream_t st);
+// dense causal GQA attention (bf16; hq/hkv divides 16)
+hipError_t launch_dense_prefill(const AttnArgs& a, hipStream_t st);
+size_t dense_decode_workspace(int B, int n_q, int hkv, int64_t n_cap);
+hipError_t launch_dense_decode(const AttnArgs& a, void* ws, hipStream_t st);
 size_t attn_decode_workspace(int B, int n_q, int hkv, int kB, int r, bool shared);
 hipError_t launch_attn_decode(qsa_dtype dt, const AttnArgs& a, void* ws, hipStream_t st);
 // Size of the fixed device array behind qsa_sparse_attn_decode_noalloc: the

@@ -22,7 +22,8 @@ EXPORTS = ["qsa_default_params", "qsa_k_blocks", "qsa_status_str", "qsa_last_err
            "qsa_index_topk_workspace",
            "qsa_sparse_attn_prefill", "qsa_sparse_attn_decode",
            "qsa_sparse_attn_decode_workspace", "qsa_sparse_attn_decode_shared",
-           "qsa_sparse_attn_decode_noalloc",
+           "qsa_sparse_attn_decode_noalloc", "qsa_dense_attn_prefill",
+           "qsa_dense_attn_decode", "qsa_dense_attn_decode_workspace",
            "qsa_probe_gather"]
 
 
@@ -84,6 +85,14 @@ def lib():
         L.qsa_sparse_attn_decode_noalloc.argtypes = [PP, ctypes.c_int, P, P, P, I64, P, P, P,
                                                      I32, I32, I32, I32, I32, F, P, P]
         L.qsa_sparse_attn_decode_noalloc.restype = ctypes.c_int
+        L.qsa_dense_attn_prefill.argtypes = [ctypes.c_int, P, P, P, I64, I32, I32, I64, I32, I32,
+                                             I32, F, P, P]
+        L.qsa_dense_attn_prefill.restype = ctypes.c_int
+        L.qsa_dense_attn_decode.argtypes = [ctypes.c_int, P, P, P, I64, P, I32, I32, I32, I32, I32,
+                                            F, P, P, SZ, P]
+        L.qsa_dense_attn_decode.restype = ctypes.c_int
+        L.qsa_dense_attn_decode_workspace.argtypes = [I32, I32, I32, I64]
+        L.qsa_dense_attn_decode_workspace.restype = SZ
         L.qsa_probe_gather.argtypes = [PP, P, P, I64, P, P, I32, I32, I64, I32, I32, I32, I32, P,
                                        P]
         L.qsa_probe_gather.restype = ctypes.c_int
@@ -205,6 +214,31 @@ def qsa_sparse_attn_decode_noalloc(p, q, k_cache, v_cache, seq_len, idx, cnt, ou
                                                 _ptr(k_cache), _ptr(v_cache), n_cap,
                                                 _ptr(seq_len), _ptr(idx), _ptr(cnt), B, n_q, hq,
                                                 hkv, d, scale, _ptr(out), _stream(stream)))
+
+
+def qsa_dense_attn_prefill(q, k, v, out, q_pos0=0, scale=0.0, stream=None):
+    """Dense causal GQA attention: q [B][n_q][hq][d] at positions q_pos0 + t,
+    k/v [B][hkv][n_cap][d] -> out [B][n_q][hq][d] (bf16)."""
+    B, n_q, hq, d = q.shape
+    hkv, n_cap = k.shape[1], k.shape[2]
+    _check(lib().qsa_dense_attn_prefill(dtype_code(q), _ptr(q), _ptr(k), _ptr(v), n_cap, B, n_q,
+                                        q_pos0, hq, hkv, d, scale, _ptr(out), _stream(stream)))
+
+
+def qsa_dense_attn_decode_workspace(B, n_q, hkv, n_cap):
+    return lib().qsa_dense_attn_decode_workspace(B, n_q, hkv, n_cap)
+
+
+def qsa_dense_attn_decode(q, k_cache, v_cache, seq_len, out, workspace, scale=0.0, stream=None):
+    """Dense causal GQA attention of n_q new tokens per sequence (positions
+    seq_len[b] - n_q + t) against the caches."""
+    B, n_q, hq, d = q.shape
+    hkv, n_cap = k_cache.shape[1], k_cache.shape[2]
+    _check(lib().qsa_dense_attn_decode(dtype_code(q), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                       n_cap, _ptr(seq_len), B, n_q, hq, hkv, d, scale,
+                                       _ptr(out), _ptr(workspace),
+                                       0 if workspace is None else workspace.numel(),
+                                       _stream(stream)))
 
 
 def qsa_probe_gather(p, k, v, idx, cnt, sink, waves_per_cu=8, depth=1, rows_per_wave=1,
