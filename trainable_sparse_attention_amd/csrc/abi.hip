@@ -377,6 +377,9 @@ static qsa_status check_dense(qsa_dtype dtype, const void* q, const void* k, con
   if (16 % (hq / hkv))
     return fail(QSA_ERR_UNSUPPORTED, "hq/hkv=%d must divide 16", hq / hkv);
   if (d != 128) return fail(QSA_ERR_UNSUPPORTED, "head dim %d: only 128", d);
+  if (n_cap > kMaxCapBf16)
+    return fail(QSA_ERR_UNSUPPORTED, "n_cap=%lld: dense attention is built for n_cap <= %lld",
+                (long long)n_cap, (long long)kMaxCapBf16);
   return QSA_OK;
 }
 

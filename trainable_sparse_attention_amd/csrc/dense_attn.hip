@@ -11,13 +11,16 @@
 // heads per KV head one 16-column MFMA group holds two tokens and nothing is
 // padded.  Each wave owns NCG groups of 16 columns.  A workgroup of W waves
 // shares one stream of 32-key K/V tiles: every tile is copied once into LDS
-// (global -> LDS, 16 bytes per lane, double-buffered) and read by all its
+// (global -> LDS, 16 bytes per lane, two tiles in flight ahead of the one
+// computed) and read by all its
 // waves.  Per tile a wave computes S^T = K Q^T (v_mfma_f32_16x16x32_bf16, 16
 // keys x 16 columns per call), an online softmax in base 2 against a
 // reference maximum that moves only when the running maximum grows by more
 // than 2^8, and O^T += V^T P^T with P kept in registers (the k index of the
 // PV call is permuted to match the S^T accumulator layout; V^T comes from
-// transposing LDS reads).
+// transposing LDS reads).  Per tile the S^T calls of all column groups come
+// first, then the softmax, then the PV calls, so that the MFMA chains are
+// independent; the column sum is kept per lane and reduced once at the end.
 //
 // Prefill: one workgroup per (sequence, KV head, tile of query tokens),
 // keys 0 .. the tile's last position.  Decode: one wave per (sequence, KV
@@ -33,6 +36,7 @@ namespace qsa {
 namespace {
 
 constexpr int kKT = 32;              // keys per tile
+constexpr int kPrefetch = 1;         // tiles loaded ahead of the computed one
 constexpr int kTileBytes = kKT * 256;  // one K or V tile in bf16
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -106,8 +110,8 @@ __global__ __launch_bounds__(64 * W) void dense_attn_kernel(AttnArgs a, int nspl
   const int64_t pos0 = nsplit == 1 ? a.q_pos0 : (int64_t)a.seq_len[b] - a.n_q;
 
   // ---- this lane's columns: token, head, position ------------------------
-  int col_t[NCG], col_h[NCG];
-  int64_t col_pos[NCG];
+  // positions stay below 2^31 (checked on the host): 32-bit compares
+  int col_t[NCG], col_h[NCG], col_pos[NCG];
   bool col_ok[NCG];
 #pragma unroll
   for (int c = 0; c < NCG; ++c) {
@@ -115,8 +119,10 @@ __global__ __launch_bounds__(64 * W) void dense_attn_kernel(AttnArgs a, int nspl
     col_t[c] = t0 + col / G;
     col_h[c] = col % G;
     col_ok[c] = col_t[c] < a.n_q && (nsplit == 1 || col < 16 * NCG);
-    col_pos[c] = pos0 + col_t[c];
+    col_pos[c] = (int)(pos0 + col_t[c]);
   }
+  // every key below this position is visible to all of the wave's columns
+  const int wave_min_pos = (int)(pos0 + t0 + (16 * NCG * wv) / G);
   // Q^T operands: column hl of group c, dims 32cc + 8gq .. + 7
   bf16x8 qf[NCG][4];
 #pragma unroll
@@ -166,23 +172,30 @@ __global__ __launch_bounds__(64 * W) void dense_attn_kernel(AttnArgs a, int nspl
     for (int tt = 0; tt < 8; ++tt) o[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // kPrefetch tiles in flight ahead of the one computed, in a ring of
+  // kPrefetch + 1 LDS buffers
   const int ntile = k_hi > k_lo ? (int)((k_hi - k_lo + kKT - 1) / kKT) : 0;
-  if (ntile > 0) issue(k_lo, smem_dense);
+  auto bufp = [&](int it) { return smem_dense + (it % (kPrefetch + 1)) * 2 * kTileBytes; };
+#pragma unroll
+  for (int j = 0; j < kPrefetch; ++j)
+    if (j < ntile) issue(k_lo + (int64_t)j * kKT, bufp(j));
   for (int it = 0; it < ntile; ++it) {
     const int64_t k0 = k_lo + (int64_t)it * kKT;
-    const unsigned char* cur = smem_dense + (it & 1) * 2 * kTileBytes;
-    // tile `it` has landed for every wave (only its loads are in flight)
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    // K operands: key row hl of 16-key tile kt, dims 32cc + 8gq
-    bf16x8 kf[2][4];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int kk = 16 * kt + hl;
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
-        kf[kt][cc] = *(const bf16x8*)(cur + kk * 256 + 16 * kswz(kk, 4 * cc + gq));
+    const unsigned char* cur = bufp(it);
+    // tile `it` has landed for every wave: this wave's later tiles (16 / W
+    // loads each) may still be in flight
+    if (it + kPrefetch - 1 < ntile) {
+      if constexpr (kPrefetch == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if constexpr (kPrefetch == 2 && W == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      if constexpr (kPrefetch == 2 && W == 8) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+      if constexpr (kPrefetch == 2 && W == 1) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      if constexpr (kPrefetch == 3 && W == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      if constexpr (kPrefetch == 3 && W == 8) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      if constexpr (kPrefetch == 3 && W == 1) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
+    __syncthreads();
     // V^T operands of O^T tile tt (dims 16tt..): k index 8gq + j <-> key
     // (j < 4 ? 4gq + j : 16 + 4gq + j - 4); lane hl reads key 4gq + hl/4
     // (+16), dims 16tt + 4(hl%4) .. + 3, transposed
@@ -198,61 +211,75 @@ __global__ __launch_bounds__(64 * W) void dense_attn_kernel(AttnArgs a, int nspl
         vr[2 * tt + 1] = lds_tr16(vs + (kk + 16) * 128 + vswz(kk + 16, c) * 8 + e0);
       }
     }
-    // the operands are in registers: the next tile may land in the other
-    // buffer while this one is computed
-    if (it + 1 < ntile) issue(k0 + kKT, smem_dense + ((it + 1) & 1) * 2 * kTileBytes);
-
+    const bool full_tile = k0 + kKT <= k_hi && k0 + kKT - 1 <= wave_min_pos;
+    // S^T of every column group first (independent MFMA chains)
+    f32x4 sacc[NCG][2];
 #pragma unroll
-    for (int c = 0; c < NCG; ++c) {
-      f32x4 sacc[2];
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int c = 0; c < NCG; ++c) sacc[c][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // K operand, read just before its calls: key row hl of 16-key tile
+        // kt, dims 32cc + 8gq
+        const int kk = 16 * kt + hl;
+        const bf16x8 kf = *(const bf16x8*)(cur + kk * 256 + 16 * kswz(kk, 4 * cc + gq));
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-          sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt][cc], qf[c][cc], sacc[kt], 0,
-                                                             0, 0);
+        for (int c = 0; c < NCG; ++c)
+          sacc[c][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c][cc], sacc[c][kt], 0,
+                                                                0, 0);
       }
-      // lane holds keys k0 + 16kt + 4gq + i of column hl
+    // every operand of this tile is in registers (V^T above, K just now): the
+    // next tile may land in another buffer while this one is computed
+    if (it + kPrefetch < ntile) issue(k0 + (int64_t)kPrefetch * kKT, bufp(it + kPrefetch));
+    bf16x8 pf[NCG];
+#pragma unroll
+    for (int c = 0; c < NCG; ++c) {
+      // lane holds keys k0 + 16kt + 4gq + i of column hl; tiles wholly below
+      // every column's position and k_hi need no mask (wave-uniform)
       float sv[8];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int64_t key = k0 + 16 * kt + 4 * gq + i;
-          const bool ok = key < k_hi && key <= col_pos[c];
-          sv[4 * kt + i] = ok ? sacc[kt][i] * sl2 : -INFINITY;
+          const int key = (int)k0 + 16 * kt + 4 * gq + i;
+          const bool ok = full_tile || (key < (int)k_hi && key <= col_pos[c]);
+          sv[4 * kt + i] = ok ? sacc[c][kt][i] * sl2 : -INFINITY;
         }
       float mx = sv[0];
 #pragma unroll
       for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
-      mx = wmax16(mx);
+      // the column's reference moves only if some lane's values exceed it
+      // by more than 2^8 (then the column maximum is formed across lanes)
       if (__ballot(mx > m[c] + 8.f)) {
-        const float mn = fmaxf(m[c], mx);
+        const float mn = fmaxf(m[c], wmax16(mx));
         const float alpha = mn == -INFINITY ? 1.f : exp2f(m[c] - mn);
         l[c] *= alpha;
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt) o[c][tt] = o[c][tt] * alpha;
         m[c] = mn;
       }
-      float rs = 0.f;
-      bf16x8 pf;
+      // l: this lane's share of the column sum (summed across lanes at the end)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float pj = sv[j] == -INFINITY ? 0.f : exp2f(sv[j] - m[c]);
-        rs += pj;
-        pf[j] = (__bf16)pj;
-      }
-      l[c] += wsum16(rs);
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        const s16x8 vv =
-            __builtin_shufflevector(vr[2 * tt], vr[2 * tt + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-        o[c][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf,
-                                                           o[c][tt], 0, 0, 0);
+        l[c] += pj;
+        pf[c][j] = (__bf16)pj;
       }
     }
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      const s16x8 vv = __builtin_shufflevector(vr[2 * tt], vr[2 * tt + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int c = 0; c < NCG; ++c)
+        o[c][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf[c],
+                                                           o[c][tt], 0, 0, 0);
+    }
   }
+#pragma unroll
+  for (int c = 0; c < NCG; ++c) l[c] = wsum16(l[c]);
 
   // ---- write out --------------------------------------------------------
   // O^T tile tt: lane (hl, gq) holds dims 16tt + 4gq .. + 3 of column hl
@@ -286,10 +313,10 @@ __global__ __launch_bounds__(64 * W) void dense_attn_kernel(AttnArgs a, int nspl
 
 // ---- host side ------------------------------------------------------------
 
-constexpr int kPrefillNCG = 4, kPrefillW = 4;
+constexpr int kPrefillNCG = 2, kPrefillW = 8;
 constexpr int kDecodeSplitKeys = 4096;
 
-static size_t dense_lds() { return 4 * (size_t)kTileBytes; }
+static size_t dense_lds() { return (kPrefetch + 1) * 2 * (size_t)kTileBytes; }
 
 hipError_t launch_dense_prefill(const AttnArgs& a, hipStream_t st) {
   const int G = a.hq / a.hkv;
