@@ -22,4 +22,7 @@ from .oracle import (  # noqa: F401
     score_at,
     attend_at,
     attend_shared,
+    attend_backward,
+    distill_rows,
+    pool_backward,
 )

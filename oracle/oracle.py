@@ -59,6 +59,12 @@ def load():
         lib.orc_attend_rows.restype = None
         lib.orc_attend_shared.argtypes = [P, P, P, I, L, L, L, P, I, I, I, I, I, D, P]
         lib.orc_attend_shared.restype = L
+        lib.orc_attend_backward.argtypes = [P, P, P, I, L, L, P, I, I, I, I, I, D, P, P, P, P]
+        lib.orc_attend_backward.restype = None
+        lib.orc_distill_row.argtypes = [P, P, I, L, I, I, I, D, P, P, I, I, I, I, D, L, P, P]
+        lib.orc_distill_row.restype = D
+        lib.orc_pool_backward.argtypes = [P, I, I, I, D, L, L, P]
+        lib.orc_pool_backward.restype = None
         lib.orc_index_at.argtypes = [P, P, I, I, I, I, I, D, I, P, L, P, P]
         lib.orc_index_at.restype = None
         lib.orc_score_at.argtypes = [P, P, I, I, I, I, I, D, P, L, P, L]
@@ -305,4 +311,68 @@ def attend_shared(q_rows, k, v, f, pos, idx_row, cnt, r=4, scale=None):
         load().orc_attend_shared(ctypes.c_void_p(base + u * step), _p(k), _p(v), dt, n_cap,
                                  int(f), p_u, _p(idx_row), int(cnt), r, hq, hkv, D, float(scale),
                                  out[u].ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+# ---- training path ---------------------------------------------------------
+
+def attend_backward(q_rows, k, v, pos, idx, cnt, dout, r=4, scale=None):
+    """Backward of the sparse attention of rows given with their positions
+    and selections: dout [m][hq][D] (float64) -> dq [m][hq][D], dk, dv
+    [hkv][n_cap][D] (float64; dk, dv summed over the rows)."""
+    q_rows, k, v = _c(q_rows), _c(k), _c(v)
+    dt = _dt(q_rows, k, v)
+    m, hq, D = q_rows.shape
+    hkv, n_cap, _ = k.shape
+    idx = _c(np.asarray(idx, dtype=np.int32))
+    cnt = _c(np.asarray(cnt, dtype=np.int32))
+    dout = _c(np.asarray(dout, dtype=np.float64))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = np.zeros((m, hq, D), dtype=np.float64)
+    dk = np.zeros((hkv, n_cap, D), dtype=np.float64)
+    dv = np.zeros((hkv, n_cap, D), dtype=np.float64)
+    step = hq * D * (2 if dt == BF16 else 4)
+    for u in range(m):
+        load().orc_attend_backward(ctypes.c_void_p(q_rows.ctypes.data + u * step), _p(k), _p(v),
+                                   dt, n_cap, int(pos[u]), idx[u].ctypes.data_as(ctypes.c_void_p),
+                                   int(cnt[u]), r, hq, hkv, D, float(scale),
+                                   dout[u].ctypes.data_as(ctypes.c_void_p),
+                                   dq[u].ctypes.data_as(ctypes.c_void_p), _p(dk), _p(dv))
+    return dq, dk, dv
+
+
+def distill_rows(q_rows, k, q_idx_rows, kbar, pos, r=4, rope_dims=64, theta=10000.0, scale=None):
+    """Indexer distillation of rows given with their positions: per-row KL of
+    the indexer's block distribution to the block-max-pooled, head-summed
+    dense attention.  q_rows [m][hq][D]; k [hkv][n_cap][D]; q_idx_rows
+    [m][h][d] (not rotated); kbar [nb_cap][d] (as stored).  Returns loss [m],
+    dq_idx [m][h][d] and dkbar [nb_cap][d] (float64, summed over the rows)."""
+    q_rows, k, q_idx_rows, kbar = _c(q_rows), _c(k), _c(q_idx_rows), _c(kbar)
+    dt = _dt(q_rows, k, q_idx_rows, kbar)
+    m, hq, D = q_rows.shape
+    hkv, n_cap, _ = k.shape
+    _, h, d = q_idx_rows.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    loss = np.zeros(m, dtype=np.float64)
+    dq = np.zeros((m, h, d), dtype=np.float64)
+    dkbar = np.zeros((kbar.shape[0], d), dtype=np.float64)
+    esz = 2 if dt == BF16 else 4
+    for u in range(m):
+        loss[u] = load().orc_distill_row(
+            ctypes.c_void_p(q_rows.ctypes.data + u * hq * D * esz), _p(k), dt, n_cap, hq, hkv, D,
+            float(scale), ctypes.c_void_p(q_idx_rows.ctypes.data + u * h * d * esz), _p(kbar), h,
+            d, r, rope_dims, float(theta), int(pos[u]), dq[u].ctypes.data_as(ctypes.c_void_p),
+            _p(dkbar))
+    return loss, dq, dkbar
+
+
+def pool_backward(dkbar, r=4, rope_dims=64, theta=10000.0, b0=0):
+    """Gradient of the raw indexer keys of blocks [b0, b0 + len) from the
+    gradient of their pooled keys: [(len) r][d] float64."""
+    dkbar = _c(np.asarray(dkbar, dtype=np.float64))
+    nbk, d = dkbar.shape
+    out = np.empty((nbk * r, d), dtype=np.float64)
+    load().orc_pool_backward(_p(dkbar), d, r, rope_dims, float(theta), b0, b0 + nbk, _p(out))
     return out

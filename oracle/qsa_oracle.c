@@ -393,3 +393,190 @@ void orc_attend_at(const void* q_rows, const void* k, const void* v, int dt, int
                out + u * (int64_t)hq * D);
   }
 }
+
+/* ------------------------------------------------------------------------
+ * Training path ([hub] "Key ideas", native-trainability bullet: stage 1
+ * distils the indexer -- KL divergence of its block scores to the teacher's
+ * block-max-pooled dense attention, the indexer trained alone -- and stage 2
+ * trains it jointly with the sparse attention).
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Backward of the sparse core attention of one query row: given the upstream
+ * gradient dout_row [hq][D] of out_row, accumulate dq_row [hq][D] (written)
+ * and dk_acc, dv_acc [hkv][n_cap][D] (added to) in double.  The selection is
+ * not differentiated (a discrete choice).  With P the softmax weights over
+ * T_i, dP_j = <dout, v_j>, Dsum = sum_j P_j dP_j, dS_j = P_j (dP_j - Dsum):
+ * dq = scale sum_j dS_j k_j, dk_j += scale dS_j q, dv_j += P_j dout.
+ */
+void orc_attend_backward(const void* q_row, const void* k, const void* v, int dt, int64_t n_cap,
+                         int64_t pos, const int32_t* idx_row, int cnt, int r, int hq, int hkv,
+                         int D, double scale, const double* dout_row, double* dq_row,
+                         double* dk_acc, double* dv_acc) {
+  int64_t nb = orc_nvis(pos, r);
+  int64_t nT = (int64_t)cnt * r + (pos + 1 - nb * r);
+  int64_t* tok = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nT > 0 ? nT : 1));
+  double* w = (double*)malloc(sizeof(double) * (size_t)(nT > 0 ? nT : 1));
+  double* dp = (double*)malloc(sizeof(double) * (size_t)(nT > 0 ? nT : 1));
+  int64_t u = 0;
+  for (int s = 0; s < cnt; ++s)
+    for (int t = 0; t < r; ++t) tok[u++] = (int64_t)idx_row[s] * r + t;
+  for (int64_t t = nb * r; t <= pos; ++t) tok[u++] = t;
+  for (int h = 0; h < hq; ++h) {
+    int g = (int)(((int64_t)h * hkv) / hq);
+    const int64_t kv0 = (int64_t)g * n_cap * D;
+    double mx = -INFINITY;
+    for (int64_t j = 0; j < nT; ++j) {
+      double dot = 0.0;
+      for (int c = 0; c < D; ++c)
+        dot += orc_ld(q_row, dt, (int64_t)h * D + c) * orc_ld(k, dt, kv0 + tok[j] * D + c);
+      w[j] = dot * scale;
+      if (w[j] > mx) mx = w[j];
+    }
+    double z = 0.0;
+    for (int64_t j = 0; j < nT; ++j) {
+      w[j] = exp(w[j] - mx);
+      z += w[j];
+    }
+    double dsum = 0.0;
+    for (int64_t j = 0; j < nT; ++j) {
+      w[j] /= z;
+      double d = 0.0;
+      for (int c = 0; c < D; ++c) d += dout_row[(int64_t)h * D + c] * orc_ld(v, dt, kv0 + tok[j] * D + c);
+      dp[j] = d;
+      dsum += w[j] * d;
+    }
+    for (int c = 0; c < D; ++c) dq_row[(int64_t)h * D + c] = 0.0;
+    for (int64_t j = 0; j < nT; ++j) {
+      double ds = w[j] * (dp[j] - dsum);
+      for (int c = 0; c < D; ++c) {
+        dq_row[(int64_t)h * D + c] += scale * ds * orc_ld(k, dt, kv0 + tok[j] * D + c);
+        dk_acc[kv0 + tok[j] * D + c] += scale * ds * orc_ld(q_row, dt, (int64_t)h * D + c);
+        dv_acc[kv0 + tok[j] * D + c] += w[j] * dout_row[(int64_t)h * D + c];
+      }
+    }
+  }
+  free(tok);
+  free(w);
+  free(dp);
+}
+
+/*
+ * Indexer distillation of one query row at position pos (stage 1).
+ *   teacher: dense causal attention of the row, p_j^h = softmax over j <= pos
+ *            of scale <q^h, k_j^{g(h)}>; block b's weight is the largest
+ *            head-summed probability among its r tokens,
+ *            a_b = max_{t<r} sum_h p_{br+t}^h, for the visible blocks
+ *            b < nb(pos); teacher distribution t_b = a_b / sum_b a_b;
+ *   student: s_b = softmax over the visible b of I_b = sum_h ReLU(<q~^h, kbar_b>)
+ *            (q~ = q_idx rotated at pos, kbar as stored);
+ *   loss:    KL(t || s) = sum_b t_b (ln t_b - ln s_b)  (0 when nb(pos) = 0).
+ * Gradients (teacher held fixed): with g_b = s_b - t_b,
+ *   dq~^h = sum_b g_b [<q~^h, kbar_b> > 0] kbar_b -> dq_idx_row = its rotation
+ *   back (angle -pos), written; dkbar_acc[b] += g_b sum_h [...] q~^h.
+ * Returns the row's loss.
+ */
+double orc_distill_row(const void* q_row, const void* k, int dt, int64_t n_cap, int hq,
+                       int hkv, int D, double scale, const void* q_idx_row, const void* kbar,
+                       int h, int d, int r, int R, double theta, int64_t pos,
+                       double* dq_idx_row, double* dkbar_acc) {
+  int64_t nb = orc_nvis(pos, r);
+  for (int c = 0; c < h * d; ++c) dq_idx_row[c] = 0.0;
+  if (nb == 0) return 0.0;
+  int64_t n = pos + 1;
+  /* teacher: head-summed probabilities of tokens 0..pos */
+  double* ps = (double*)calloc((size_t)n, sizeof(double));
+  double* w = (double*)malloc(sizeof(double) * (size_t)n);
+  for (int hh = 0; hh < hq; ++hh) {
+    int g = (int)(((int64_t)hh * hkv) / hq);
+    const int64_t kv0 = (int64_t)g * n_cap * D;
+    double mx = -INFINITY;
+    for (int64_t j = 0; j < n; ++j) {
+      double dot = 0.0;
+      for (int c = 0; c < D; ++c)
+        dot += orc_ld(q_row, dt, (int64_t)hh * D + c) * orc_ld(k, dt, kv0 + j * D + c);
+      w[j] = dot * scale;
+      if (w[j] > mx) mx = w[j];
+    }
+    double z = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+      w[j] = exp(w[j] - mx);
+      z += w[j];
+    }
+    for (int64_t j = 0; j < n; ++j) ps[j] += w[j] / z;
+  }
+  double* a = (double*)malloc(sizeof(double) * (size_t)nb);
+  double asum = 0.0;
+  for (int64_t b = 0; b < nb; ++b) {
+    double m = ps[b * r];
+    for (int t = 1; t < r; ++t)
+      if (ps[b * r + t] > m) m = ps[b * r + t];
+    a[b] = m;
+    asum += m;
+  }
+  /* student */
+  double* q = (double*)malloc(sizeof(double) * (size_t)(h * d));
+  for (int c = 0; c < h * d; ++c) q[c] = orc_ld(q_idx_row, dt, c);
+  for (int hh = 0; hh < h; ++hh) orc_rope(q + hh * d, R, theta, (double)pos);
+  double* I = (double*)malloc(sizeof(double) * (size_t)nb);
+  unsigned char* pos_dot = (unsigned char*)malloc((size_t)(nb * h));
+  double imax = -INFINITY;
+  for (int64_t b = 0; b < nb; ++b) {
+    double s = 0.0;
+    for (int hh = 0; hh < h; ++hh) {
+      double dot = 0.0;
+      for (int c = 0; c < d; ++c) dot += q[hh * d + c] * orc_ld(kbar, dt, b * (int64_t)d + c);
+      pos_dot[b * h + hh] = dot > 0.0;
+      s += dot > 0.0 ? dot : 0.0;
+    }
+    I[b] = s;
+    if (s > imax) imax = s;
+  }
+  double zs = 0.0;
+  for (int64_t b = 0; b < nb; ++b) zs += exp(I[b] - imax);
+  double lz = imax + log(zs); /* ln sum_b exp(I_b) */
+  double loss = 0.0;
+  double* dq = (double*)calloc((size_t)(h * d), sizeof(double));
+  for (int64_t b = 0; b < nb; ++b) {
+    double t = a[b] / asum;
+    double ls = I[b] - lz;
+    if (t > 0.0) loss += t * (log(t) - ls);
+    double gb = exp(ls) - t;
+    for (int hh = 0; hh < h; ++hh) {
+      if (!pos_dot[b * h + hh]) continue;
+      for (int c = 0; c < d; ++c) {
+        dq[hh * d + c] += gb * orc_ld(kbar, dt, b * (int64_t)d + c);
+        dkbar_acc[b * (int64_t)d + c] += gb * q[hh * d + c];
+      }
+    }
+  }
+  /* back through the rotation: rotate by -pos */
+  for (int hh = 0; hh < h; ++hh) orc_rope(dq + hh * d, R, theta, -(double)pos);
+  for (int c = 0; c < h * d; ++c) dq_idx_row[c] = dq[c];
+  free(ps);
+  free(w);
+  free(a);
+  free(q);
+  free(I);
+  free(pos_dot);
+  free(dq);
+  return loss;
+}
+
+/*
+ * Backward of the pooling (orc_pool): the gradient of the raw indexer keys
+ * of blocks [b0, b1) given the gradient dkbar [(b1-b0)][d] of the pooled
+ * keys: each of the block's r keys receives (1/r) times dkbar rotated back
+ * (angle -(b+1)r+1).  dk_out: [(b1-b0) r][d], written.
+ */
+void orc_pool_backward(const double* dkbar, int d, int r, int R, double theta, int64_t b0,
+                       int64_t b1, double* dk_out) {
+  double* m = (double*)malloc(sizeof(double) * (size_t)d);
+  for (int64_t b = b0; b < b1; ++b) {
+    for (int c = 0; c < d; ++c) m[c] = dkbar[(b - b0) * (int64_t)d + c];
+    orc_rope(m, R, theta, -(double)((b + 1) * r - 1));
+    for (int t = 0; t < r; ++t)
+      for (int c = 0; c < d; ++c) dk_out[((b - b0) * r + t) * (int64_t)d + c] = m[c] / (double)r;
+  }
+  free(m);
+}

@@ -1,0 +1,192 @@
+"""Pins of the oracle's training path ([hub] "Key ideas", native-trainability
+bullet: stage 1 distils the indexer to the block-max-pooled teacher
+attention with a KL loss, stage 2 trains it jointly with the sparse
+attention).
+
+Each gradient is pinned by central finite differences of the oracle's own
+forward (inputs chosen exactly representable, steps exact in float32), and by
+a library routine or a closed form where one exists: torch autograd of
+float64 causal SDPA when every block is selected, the teacher and the KL
+written out with numpy for one head at r = 1 and two heads at r = 2 (head
+sum, then the block's largest token), the adjoint identity of the pooling.
+"""
+import math
+
+import numpy as np
+import torch
+
+import oracle
+from trainable_sparse_attention_amd import inputs
+
+
+def _grid(rng, shape, bits=8, spread=1.0):
+    """float32 values that are multiples of 2^-bits (exact under +- 2^-14)."""
+    x = np.round(rng.standard_normal(shape) * spread * 2 ** bits) / 2 ** bits
+    return x.astype(np.float32)
+
+
+def _fd(f, arr, ix, eps=2.0 ** -14):
+    old = arr[ix]
+    arr[ix] = old + np.float32(eps)
+    hi = f()
+    arr[ix] = old - np.float32(eps)
+    lo = f()
+    arr[ix] = old
+    return (hi - lo) / (2 * eps)
+
+
+def _sample_ix(rng, shape, k):
+    return [tuple(int(rng.integers(0, s)) for s in shape) for _ in range(k)]
+
+
+# ---- stage 2: sparse attention backward ------------------------------------
+
+def test_attend_backward_finite_differences():
+    rng = np.random.default_rng(31)
+    n, r, K, hq, hkv, D = 40, 4, 16, 4, 2, 128
+    q = _grid(rng, (n, hq, D), spread=0.3)
+    k = _grid(rng, (hkv, n, D), spread=0.3)
+    v = _grid(rng, (hkv, n, D))
+    q_idx = _grid(rng, (n, 4, 128), spread=0.1)
+    kbar = oracle.pool(_grid(rng, (n, 128), spread=0.1), r=r)
+    rows = np.arange(n)
+    idx, cnt = oracle.index_rows(q_idx, kbar, rows, r=r, K=K)
+    assert cnt.max() < (n + 1) // r  # some rows are sparse
+    w = rng.standard_normal((n, hq, D))
+
+    def loss():
+        return float(np.sum(w * oracle.attend_at(q, k, v, rows, idx, cnt, r=r)))
+
+    dq, dk, dv = oracle.attend_backward(q, k, v, rows, idx, cnt, w, r=r)
+    for arr, grad in ((q, dq), (k, dk), (v, dv)):
+        for ix in _sample_ix(rng, arr.shape, 24):
+            fd = _fd(loss, arr, ix)
+            assert abs(fd - grad[ix]) <= 1e-6 + 1e-5 * abs(grad[ix]), (ix, fd, grad[ix])
+
+
+def test_attend_backward_every_block_is_dense_autograd():
+    """K >= n: each row attends to 0..i, so the gradients are those of causal
+    attention -- torch autograd through float64 SDPA, KV heads repeated."""
+    rng = np.random.default_rng(32)
+    n, r, hq, hkv, D = 37, 4, 8, 2, 128
+    d = inputs.small(n=n, hq=hq, hkv=hkv, r=r, K=4096, seed=33)
+    q, k, v = d["q"][0], d["k"][0], d["v"][0]
+    kbar = oracle.pool(d["k_idx"][0], r=r)
+    rows = np.arange(n)
+    idx, cnt = oracle.index_rows(d["q_idx"][0], kbar, rows, r=r, K=4096)
+    w = rng.standard_normal((n, hq, D))
+    dq, dk, dv = oracle.attend_backward(q, k, v, rows, idx, cnt, w, r=r)
+    qt = torch.from_numpy(q.astype(np.float64)).permute(1, 0, 2)[None].requires_grad_()
+    kt = torch.from_numpy(k.astype(np.float64))[None].requires_grad_()
+    vt = torch.from_numpy(v.astype(np.float64))[None].requires_grad_()
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt.repeat_interleave(hq // hkv, 1), vt.repeat_interleave(hq // hkv, 1), is_causal=True)
+    (o * torch.from_numpy(w).permute(1, 0, 2)[None]).sum().backward()
+    np.testing.assert_allclose(dq, qt.grad[0].permute(1, 0, 2).numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk, kt.grad[0].numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv, vt.grad[0].numpy(), rtol=1e-10, atol=1e-12)
+
+
+# ---- stage 1: indexer distillation ------------------------------------------
+
+def test_distill_finite_differences():
+    """Gradients of the summed KL w.r.t. the raw (unrotated) indexer queries
+    and the pooled keys; the teacher is held fixed (it does not depend on
+    them)."""
+    rng = np.random.default_rng(34)
+    n, r, hq, hkv, D = 48, 4, 4, 2, 128
+    q = _grid(rng, (n, hq, D), spread=0.5)
+    k = _grid(rng, (hkv, n, D), spread=0.5)
+    q_idx = _grid(rng, (n, 4, 128), spread=0.2)
+    kbar = _grid(rng, (n // r, 128), spread=0.2)
+    pos = np.arange(n)
+
+    def loss():
+        return float(oracle.distill_rows(q, k, q_idx, kbar, pos, r=r)[0].sum())
+
+    L, dq, dkb = oracle.distill_rows(q, k, q_idx, kbar, pos, r=r)
+    assert np.all(L >= -1e-12) and L[:r - 1].max() == 0.0  # no visible block: no loss
+    for arr, grad in ((q_idx, dq), (kbar, dkb)):
+        for ix in _sample_ix(rng, arr.shape, 32):
+            fd = _fd(loss, arr, ix)
+            assert abs(fd - grad[ix]) <= 1e-7 + 1e-5 * abs(grad[ix]), (ix, fd, grad[ix])
+
+
+def test_distill_single_head_r1_is_softmax_kl():
+    """One attention head and r = 1: every block is one token, so the teacher
+    is the attention distribution itself; the loss is KL(p || softmax(I))
+    written out here with numpy."""
+    rng = np.random.default_rng(35)
+    n, D = 30, 128
+    q = _grid(rng, (n, 1, D), spread=0.6)
+    k = _grid(rng, (1, n, D), spread=0.6)
+    q_idx = _grid(rng, (n, 4, 128), spread=0.2)
+    kbar = _grid(rng, (n, 128), spread=0.2)
+    pos = np.arange(n)
+    L, _, _ = oracle.distill_rows(q, k, q_idx, kbar, pos, r=1)
+    for i in range(n):
+        lg = (k[0, :i + 1].astype(np.float64) @ q[i, 0].astype(np.float64)) / math.sqrt(D)
+        p = np.exp(lg - lg.max())
+        p /= p.sum()
+        I = oracle.scores(q_idx[i], kbar, i, r=1)
+        ls = I - (I.max() + np.log(np.exp(I - I.max()).sum()))
+        ref = float(np.sum(p * (np.log(p) - ls)))
+        assert abs(L[i] - ref) <= 1e-12 + 1e-10 * abs(ref), (i, L[i], ref)
+
+
+def test_distill_teacher_is_head_sum_block_max():
+    """Two attention heads on two KV heads, r = 2: the teacher weight of a
+    block is the larger of its two tokens' head-summed probabilities,
+    normalised over the visible blocks -- written out here with numpy."""
+    rng = np.random.default_rng(38)
+    n, D, r, hq, hkv = 26, 128, 2, 2, 2
+    q = _grid(rng, (n, hq, D), spread=0.6)
+    k = _grid(rng, (hkv, n, D), spread=0.6)
+    q_idx = _grid(rng, (n, 4, 128), spread=0.2)
+    kbar = _grid(rng, (n // r, 128), spread=0.2)
+    pos = np.arange(n)
+    L, _, _ = oracle.distill_rows(q, k, q_idx, kbar, pos, r=r)
+    for i in range(n):
+        nb = (i + 1) // r
+        if nb == 0:
+            assert L[i] == 0.0
+            continue
+        ps = np.zeros(i + 1)
+        for h in range(hq):
+            lg = (k[h, :i + 1].astype(np.float64) @ q[i, h].astype(np.float64)) / math.sqrt(D)
+            p = np.exp(lg - lg.max())
+            ps += p / p.sum()
+        a = np.maximum(ps[0:2 * nb:2], ps[1:2 * nb:2])
+        t = a / a.sum()
+        I = oracle.scores(q_idx[i], kbar, i, r=r)
+        ls = I - (I.max() + np.log(np.exp(I - I.max()).sum()))
+        ref = float(np.sum(t * (np.log(t) - ls)))
+        assert abs(L[i] - ref) <= 1e-12 + 1e-10 * abs(ref), (i, L[i], ref)
+
+
+def test_distill_one_visible_block_has_no_loss():
+    """With one visible block both distributions are that block: loss and
+    gradients are zero."""
+    rng = np.random.default_rng(36)
+    q = _grid(rng, (8, 4, 128))
+    k = _grid(rng, (2, 8, 128))
+    q_idx = _grid(rng, (8, 4, 128))
+    kbar = _grid(rng, (2, 128))
+    pos = np.array([3, 4, 5, 6])  # each sees block 0 only
+    L, dq, dkb = oracle.distill_rows(q[pos], k, q_idx[pos], kbar, pos, r=4)
+    assert np.all(L == 0.0) and np.all(dq == 0.0) and np.all(dkb == 0.0)
+
+
+def test_pool_backward_is_the_adjoint_of_pooling():
+    """<w, pool(k)> = <pool_backward(w), k> (pooling and rotation are linear;
+    float32 storage of the pooled keys bounds the difference)."""
+    rng = np.random.default_rng(37)
+    n, r = 256, 4
+    kin = rng.standard_normal((n, 128)).astype(np.float32)
+    w = rng.standard_normal((n // r, 128))
+    for b0 in (0, 17):
+        pk = oracle.pool(kin, r=r, b0=b0, b1=n // r).astype(np.float64)
+        lhs = float(np.sum(w[b0:] * pk))
+        dk = oracle.pool_backward(w[b0:], r=r, b0=b0)
+        rhs = float(np.sum(dk * kin[b0 * r:].astype(np.float64)))
+        assert abs(lhs - rhs) <= 1e-6 * np.sum(np.abs(w[b0:] * pk)), (lhs, rhs)
