@@ -259,6 +259,71 @@ qsa_status qsa_sparse_attn_decode_noalloc(const qsa_params* p, qsa_dtype dtype, 
                                           float scale, void* out, void* stream);
 
 /*
+ * qsa_sparse_attn_backward -- gradients of the sparse core attention for
+ * joint sparse training ([hub] "Key ideas": stage 2 trains the indexer and
+ * the sparse attention together).  The block selection (idx, cnt, as given
+ * to qsa_sparse_attn_prefill for the same rows) is a discrete choice and
+ * gets no gradient.  With P the softmax weights of row t over T_t:
+ *   dP_j = <dout, v_j>, Dsum = <dout, out>, dS_j = P_j (dP_j - Dsum),
+ *   dq = scale sum_j dS_j k_j,  dk_j += scale dS_j q,  dv_j += P_j dout.
+ *
+ *   q, out, dout : [B][n_q][hq][d] bfloat16 (out as the forward wrote it);
+ *   k, v : [B][hkv][n_cap][d] bfloat16;
+ *   dq : [B][n_q][hq][d] float32, written;
+ *   dk, dv : [B][hkv][n_cap][d] float32, ADDED to (the caller clears them;
+ *            rows attended by no query are left untouched)
+ * Errors as for qsa_sparse_attn_prefill; float32 inputs ->
+ * QSA_ERR_UNSUPPORTED.
+ */
+qsa_status qsa_sparse_attn_backward(const qsa_params* p, qsa_dtype dtype, const void* q,
+                                    const void* k, const void* v, int64_t n_cap,
+                                    const int32_t* idx, const int32_t* cnt, const void* out,
+                                    const void* dout, int32_t B, int32_t n_q, int64_t q_pos0,
+                                    int32_t hq, int32_t hkv, int32_t d, float scale, float* dq,
+                                    float* dk, float* dv, void* stream);
+
+/*
+ * qsa_index_distill -- stage-1 indexer distillation ([hub] "Key ideas",
+ * native-trainability bullet: KL divergence of the indexer's scores to the
+ * teacher's dense attention max-pooled over micro-blocks, the indexer
+ * trained alone).  For query row t at position p = q_pos0 + t with
+ * nb = floor((p+1)/r) complete blocks:
+ *   teacher  a_b = max over the block's r tokens of sum_h softmax_{j<=p}(
+ *            scale <q^h, k_j^{g(h)}>), normalised over b < nb;
+ *   student  softmax over b < nb of I_b = sum_h ReLU(<q~^h, kbar_b>)
+ *            (q~ = q_idx rotated at p, kbar as stored);
+ *   loss[t]  = KL(teacher || student)  (0 when nb = 0);
+ *   dq_idx   gradient of loss[t] w.r.t. the row's raw indexer queries
+ *            (teacher fixed), written;
+ *   dkbar    gradient of sum_t loss[t] w.r.t. the pooled keys, ADDED to.
+ *
+ *   q : [B][n_q][hq][d] bfloat16; k : [B][hkv][n_cap][d] bfloat16 (the
+ *   attention keys); q_idx : [B][n_q][4][128] and kbar : [B][nb_cap][128]
+ *   bfloat16; loss : [B][n_q], dq_idx : [B][n_q][4][128], dkbar :
+ *   [B][nb_cap][128], all float32.  Built for r = 4, rope_dims <= 64,
+ *   hq <= 16, hkv <= 8, d = 128.
+ * Errors: NULL pointers; positions beyond n_cap or seeing more than nb_cap
+ * blocks -> QSA_ERR_SHAPE; other dtypes or sizes -> QSA_ERR_UNSUPPORTED.
+ */
+qsa_status qsa_index_distill(const qsa_params* p, qsa_dtype dtype, const void* q, const void* k,
+                             int64_t n_cap, const void* q_idx, const void* kbar, int64_t nb_cap,
+                             int32_t B, int32_t n_q, int64_t q_pos0, int32_t hq, int32_t hkv,
+                             int32_t d, float scale, float* loss, float* dq_idx, float* dkbar,
+                             void* stream);
+
+/*
+ * qsa_pool_keys_backward -- gradient of the raw indexer keys from the
+ * gradient of the pooled keys (qsa_pool_keys is linear: each of block j's r
+ * keys receives (1/r) times dkbar[j] rotated back by the block's angle).
+ *   dkbar : [B][nb_cap][d_idx] float32; dk_idx : [B][n_cap][d_idx] float32,
+ *   rows of blocks [block_begin, block_end) written.
+ * Errors as for qsa_pool_keys.
+ */
+qsa_status qsa_pool_keys_backward(const qsa_params* p, const float* dkbar, int64_t nb_cap,
+                                  float* dk_idx, int64_t n_cap, int32_t B, int64_t block_begin,
+                                  int64_t block_end, void* stream);
+
+/*
  * qsa_dense_attn_prefill -- dense causal GQA attention: every query attends
  * to all tokens 0 .. its position.  This is QSA with every block selected
  * (k_B at least the visible blocks), and the dense baseline of the pages'

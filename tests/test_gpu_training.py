@@ -1,0 +1,113 @@
+"""GPU parity of the training path against the oracle ([hub] "Key ideas",
+native-trainability bullet): the sparse-attention backward (stage 2, joint
+sparse training), the indexer distillation loss and its gradients (stage 1),
+and the pooling backward that carries the pooled-key gradient to the raw
+indexer keys.
+
+Tolerances: gradients and losses are accumulated in float32 from bf16
+inputs (the attention backward rounds P and dS to bf16 for its MFMA
+products, as the forward rounds P), so outputs are compared with the
+max-abs relative error of the bf16 class, 2e-2, and the distillation
+(float32 throughout, the student's query carried as bf16 hi + lo) with
+2e-3.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.parity import TOL, rel_err, to_dev, to_host
+from trainable_sparse_attention_amd import inputs, qsa
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+def _bf16(x):
+    return inputs.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+@pytest.mark.parametrize("r,n,K,q_pos0", [(4, 1200, 256, 0), (8, 1500, 512, 0),
+                                          (4, 2000, 512, 1300)])
+def test_sparse_attn_backward(r, n, K, q_pos0):
+    say("sparse attention backward r=%d n=%d K=%d q_pos0=%d" % (r, n, K, q_pos0))
+    B, hq, hkv = 2, 16, 2
+    d = inputs.small(B=B, n=n, hq=hq, hkv=hkv, dtype="bf16", r=r, K=K, seed=600 + r)
+    p = qsa.params(r=r, K=K)
+    kB = qsa.k_blocks(p)
+    t = {k_: to_dev(d[k_]) for k_ in ("q_idx", "k_idx", "q", "k", "v")}
+    nb = n // r
+    kbar = torch.empty((B, nb, 128), dtype=torch.bfloat16, device="cuda")
+    qsa.qsa_pool_keys(p, t["k_idx"], kbar, 0, nb)
+    n_q = n - q_pos0
+    qi = t["q_idx"][:, q_pos0:].contiguous()
+    qq = t["q"][:, q_pos0:].contiguous()
+    idx = torch.empty((B, n_q, kB), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, n_q), dtype=torch.int32, device="cuda")
+    ws = qsa.workspace(qsa.qsa_index_topk_workspace(p, qsa.QSA_BF16, B, n_q, nb, False))
+    qsa.qsa_index_topk(p, qi, kbar, idx, cnt, ws, q_pos0)
+    out = torch.empty_like(qq)
+    qsa.qsa_sparse_attn_prefill(p, qq, t["k"], t["v"], idx, cnt, out, q_pos0)
+    rng = np.random.default_rng(7)
+    dout_h = _bf16(rng.standard_normal((B, n_q, hq, 128)) * 0.1)
+    dout = to_dev(dout_h)
+    dq = torch.empty((B, n_q, hq, 128), dtype=torch.float32, device="cuda")
+    dk = torch.zeros((B, hkv, n, 128), dtype=torch.float32, device="cuda")
+    dv = torch.zeros_like(dk)
+    qsa.qsa_sparse_attn_backward(p, qq, t["k"], t["v"], idx, cnt, out, dout, dq, dk, dv, q_pos0)
+    torch.cuda.synchronize()
+    g_idx, g_cnt = to_host(idx), to_host(cnt)
+    g_dq, g_dk, g_dv = dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+    pos = q_pos0 + np.arange(n_q)
+    for b in range(B):
+        dout_f = inputs.bf16_bits_to_f32(dout_h[b]).astype(np.float64)
+        o_dq, o_dk, o_dv = oracle.attend_backward(d["q"][b][pos], d["k"][b], d["v"][b], pos,
+                                                  g_idx[b], g_cnt[b], dout_f, r=r)
+        errs = [rel_err(g_dq[b], o_dq), rel_err(g_dk[b], o_dk), rel_err(g_dv[b], o_dv)]
+        say("seq %d: dq %.2e dk %.2e dv %.2e" % (b, *errs))
+        assert max(errs) <= TOL["bf16"]
+        # key rows no query attended keep their cleared value
+        untouched = np.all(o_dk == 0.0, axis=2)
+        assert np.all(g_dk[b][untouched] == 0.0) and np.all(g_dv[b][untouched] == 0.0)
+
+
+@pytest.mark.parametrize("n,q_pos0,hq,hkv", [(1000, 0, 16, 2), (1500, 900, 16, 2),
+                                             (777, 0, 8, 1)])
+def test_index_distill(n, q_pos0, hq, hkv):
+    say("distillation n=%d q_pos0=%d hq=%d hkv=%d" % (n, q_pos0, hq, hkv))
+    B = 2
+    d = inputs.small(B=B, n=n, hq=hq, hkv=hkv, dtype="bf16", seed=700 + n, planted=0)
+    p = qsa.params()
+    t = {k_: to_dev(d[k_]) for k_ in ("q_idx", "k_idx", "q", "k")}
+    nb = n // 4
+    kbar = torch.empty((B, nb, 128), dtype=torch.bfloat16, device="cuda")
+    qsa.qsa_pool_keys(p, t["k_idx"], kbar, 0, nb)
+    n_q = n - q_pos0
+    qq = t["q"][:, q_pos0:].contiguous()
+    qi = t["q_idx"][:, q_pos0:].contiguous()
+    loss = torch.full((B, n_q), -1.0, dtype=torch.float32, device="cuda")
+    dq = torch.empty((B, n_q, 4, 128), dtype=torch.float32, device="cuda")
+    dkb = torch.zeros((B, nb, 128), dtype=torch.float32, device="cuda")
+    qsa.qsa_index_distill(p, qq, t["k"], qi, kbar, loss, dq, dkb, q_pos0)
+    # the pooled-key gradient carried to the raw indexer keys
+    dk_idx = torch.zeros((B, n, 128), dtype=torch.float32, device="cuda")
+    qsa.qsa_pool_keys_backward(p, dkb, dk_idx, 0, nb)
+    torch.cuda.synchronize()
+    kbar_h = to_host(kbar)
+    g_loss, g_dq, g_dkb, g_dk = (x.cpu().numpy() for x in (loss, dq, dkb, dk_idx))
+    pos = q_pos0 + np.arange(n_q)
+    for b in range(B):
+        o_loss, o_dq, o_dkb = oracle.distill_rows(d["q"][b][pos], d["k"][b], d["q_idx"][b][pos],
+                                                  kbar_h[b], pos)
+        errs = [rel_err(g_loss[b], o_loss), rel_err(g_dq[b], o_dq), rel_err(g_dkb[b], o_dkb)]
+        say("seq %d: loss %.2e dq_idx %.2e dkbar %.2e (mean loss %.4f)" % (b, *errs,
+                                                                         float(o_loss.mean())))
+        assert max(errs) <= 2e-3
+        assert np.all(g_loss[b][pos < 3] == 0.0)
+        o_dk = oracle.pool_backward(g_dkb[b].astype(np.float64))
+        assert rel_err(g_dk[b][:nb * 4], o_dk) <= 1e-6

@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libqsa.so")
 SOURCES = ["abi.hip", "pool_keys.hip", "index_prefill.hip", "index_exact.hip", "index_decode.hip",
-           "attn.hip", "dense_attn.hip", "probe_gather.hip"]
+           "attn.hip", "attn_bwd.hip", "distill.hip", "dense_attn.hip", "probe_gather.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Wno-unused-function", "-Wno-unused-variable",
@@ -20,7 +20,9 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # per-file additions: the attention kernels keep MFMA accumulators in VGPRs,
 # where the online-softmax rescale can scale them without AGPR round trips
-EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         # float atomics of the gradient scatter as hardware adds
+         "attn_bwd.hip": ["-munsafe-fp-atomics"], "distill.hip": ["-munsafe-fp-atomics"]}
 
 
 def _compile(src, obj):

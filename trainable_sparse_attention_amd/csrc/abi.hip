@@ -364,6 +364,103 @@ qsa_status qsa_sparse_attn_decode_noalloc(const qsa_params* p, qsa_dtype dtype, 
                   "sparse_attn_decode_noalloc");
 }
 
+qsa_status qsa_sparse_attn_backward(const qsa_params* p, qsa_dtype dtype, const void* q,
+                                    const void* k, const void* v, int64_t n_cap,
+                                    const int32_t* idx, const int32_t* cnt, const void* out,
+                                    const void* dout, int32_t B, int32_t n_q, int64_t q_pos0,
+                                    int32_t hq, int32_t hkv, int32_t d, float scale, float* dq,
+                                    float* dk, float* dv, void* stream) {
+  qsa_status s = check_attn(p, dtype, q, k, v, idx, cnt, dq, B, n_q, hq, hkv, d, n_cap);
+  if (s) return s;
+  if (dtype != QSA_BF16) return fail(QSA_ERR_UNSUPPORTED, "the backward is built for bf16");
+  if (!out || !dout || !dk || !dv) return fail(QSA_ERR_NULL, "NULL tensor argument");
+  if (q_pos0 < 0 || q_pos0 + n_q > n_cap)
+    return fail(QSA_ERR_SHAPE, "positions [%lld, %lld) exceed n_cap=%lld", (long long)q_pos0,
+                (long long)(q_pos0 + n_q), (long long)n_cap);
+  if (B == 0) return QSA_OK;
+  AttnArgs a = {};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = const_cast<void*>(out);
+  a.idx = idx;
+  a.cnt = cnt;
+  a.n_cap = n_cap;
+  a.q_pos0 = q_pos0;
+  a.B = B;
+  a.n_q = n_q;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.kB = qsa_k_blocks(p);
+  a.r = p->r;
+  a.scale = scale > 0.f ? scale : 1.f / sqrtf((float)d);
+  return launched(launch_attn_backward(a, dout, dq, dk, dv, (hipStream_t)stream),
+                  "sparse_attn_backward");
+}
+
+qsa_status qsa_index_distill(const qsa_params* p, qsa_dtype dtype, const void* q, const void* k,
+                             int64_t n_cap, const void* q_idx, const void* kbar, int64_t nb_cap,
+                             int32_t B, int32_t n_q, int64_t q_pos0, int32_t hq, int32_t hkv,
+                             int32_t d, float scale, float* loss, float* dq_idx, float* dkbar,
+                             void* stream) {
+  qsa_status s = check_params(p);
+  if (s) return s;
+  if ((s = check_dtype(dtype))) return s;
+  if (dtype != QSA_BF16) return fail(QSA_ERR_UNSUPPORTED, "distillation is built for bf16");
+  if (p->r != 4) return fail(QSA_ERR_UNSUPPORTED, "distillation is built for r = 4");
+  if (p->rope_dims > 64) return fail(QSA_ERR_UNSUPPORTED, "distillation: rope_dims <= 64");
+  if (!q || !k || !q_idx || !kbar || !loss || !dq_idx || !dkbar)
+    return fail(QSA_ERR_NULL, "NULL tensor argument");
+  if (B < 0 || n_q < 1 || hq < 1 || hkv < 1 || n_cap < 1 || nb_cap < 0)
+    return fail(QSA_ERR_SHAPE, "B>=0, n_q>=1, hq>=1, hkv>=1, n_cap>=1, nb_cap>=0");
+  if (hq % hkv) return fail(QSA_ERR_SHAPE, "hq=%d not a multiple of hkv=%d", hq, hkv);
+  if (hq > 16 || hkv > 8) return fail(QSA_ERR_UNSUPPORTED, "distillation: hq <= 16, hkv <= 8");
+  if (d != 128) return fail(QSA_ERR_UNSUPPORTED, "head dim %d: only 128", d);
+  if (q_pos0 < 0 || q_pos0 + n_q > n_cap)
+    return fail(QSA_ERR_SHAPE, "positions [%lld, %lld) exceed n_cap=%lld", (long long)q_pos0,
+                (long long)(q_pos0 + n_q), (long long)n_cap);
+  if ((q_pos0 + n_q) / p->r > nb_cap)
+    return fail(QSA_ERR_SHAPE, "positions see more blocks than nb_cap=%lld", (long long)nb_cap);
+  if (n_cap > kMaxCapBf16 || q_pos0 + n_q > (int64_t)0x7fffffff)
+    return fail(QSA_ERR_UNSUPPORTED, "n_cap beyond %lld", (long long)kMaxCapBf16);
+  if (B == 0) return QSA_OK;
+  DistillArgs a;
+  a.q = (const unsigned short*)q;
+  a.k = (const unsigned short*)k;
+  a.q_idx = (const unsigned short*)q_idx;
+  a.kbar = (const unsigned short*)kbar;
+  a.loss = loss;
+  a.dq_idx = dq_idx;
+  a.dkbar = dkbar;
+  a.n_cap = n_cap;
+  a.nb_cap = nb_cap;
+  a.q_pos0 = q_pos0;
+  a.B = B;
+  a.n_q = n_q;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.R = p->rope_dims;
+  a.scale = scale > 0.f ? scale : 1.f / sqrtf((float)d);
+  a.log2_theta = log2((double)p->rope_theta);
+  return launched(launch_distill(a, (hipStream_t)stream), "index_distill");
+}
+
+qsa_status qsa_pool_keys_backward(const qsa_params* p, const float* dkbar, int64_t nb_cap,
+                                  float* dk_idx, int64_t n_cap, int32_t B, int64_t block_begin,
+                                  int64_t block_end, void* stream) {
+  qsa_status s = check_params(p);
+  if (s) return s;
+  if (!dkbar || !dk_idx) return fail(QSA_ERR_NULL, "dkbar or dk_idx is NULL");
+  if (B < 0 || n_cap < 0 || nb_cap < 0 || block_begin < 0 || block_begin > block_end)
+    return fail(QSA_ERR_SHAPE, "bad sizes or block range");
+  if (block_end * (int64_t)p->r > n_cap || block_end > nb_cap)
+    return fail(QSA_ERR_SHAPE, "block range beyond n_cap or nb_cap");
+  return launched(launch_pool_backward(dkbar, nb_cap, dk_idx, n_cap, B, block_begin, block_end,
+                                       p->r, p->rope_dims, log2((double)p->rope_theta),
+                                       (hipStream_t)stream),
+                  "pool_keys_backward");
+}
+
 static qsa_status check_dense(qsa_dtype dtype, const void* q, const void* k, const void* v,
                               void* out, int32_t B, int32_t n_q, int32_t hq, int32_t hkv,
                               int32_t d, int64_t n_cap) {

@@ -1,0 +1,443 @@
+// Indexer distillation loss and its gradients (research-hub note, "Key
+// ideas", native-trainability bullet: stage 1 trains the indexer alone on a
+// KL divergence to the teacher's dense attention, max-pooled over each
+// micro-block).
+//
+// For query row i (position p, nb = floor((p+1)/4) complete blocks):
+//   teacher  P_j^h = softmax_{j <= p}(scale <q^h, k_j^{g(h)}>),
+//            a_b = max_{t<4} sum_h P_{4b+t}^h,  t_b = a_b / sum_b a_b  (b < nb)
+//   student  I_b = sum_{h<4} ReLU(<q~^h, kbar_b>),  s_b = softmax_{b < nb}(I_b)
+//   loss     KL(t || s);  g_b = s_b - t_b
+//   grads    dq~^h = sum_b g_b [<q~^h, kbar_b> > 0] kbar_b (rotated back to
+//            dq_idx), dkbar_b += g_b sum_h [...] q~^h.
+//
+// A workgroup of 8 waves takes 8 consecutive rows (one wave each) and walks
+// the history in lock step, 64 keys (16 blocks) a step; each step's K rows of
+// every KV head and the 16 pooled keys are copied once into LDS.  Per wave:
+// teacher logits S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (16 columns = the
+// query heads, one call per KV head, each column keeping its own head's
+// product), student scores on the same MFMA with the rotated indexer
+// queries carried as bf16 hi + lo (float-level accuracy), head sums and the
+// block maximum by lane shuffles.  Three passes over the history: the
+// teacher's log-sum-exp per head; the normalisers (sum of a_b, the
+// student's log-sum-exp) and the loss; the gradients.  dkbar is summed over
+// the workgroup's rows in LDS and added to global memory with float atomics.
+//
+// Built for r = 4, bfloat16 inputs, hq <= 16, 4 indexer heads of 128 dims,
+// rope_dims <= 64.
+#include <math.h>
+
+#include "index_common.h"
+
+namespace qsa {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+constexpr int kDW = 8;         // waves (rows) per workgroup
+constexpr int kStepKeys = 64;  // keys per step
+constexpr int kStepBlk = 16;   // blocks per step (r = 4)
+constexpr int kMaxKv = 16;
+
+__device__ __forceinline__ int dswz(int kk, int c) { return c ^ (kk & 15); }
+
+__device__ __forceinline__ float xsum16(float x) {  // over the 16 lanes of a group
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 4);
+  return x + __shfl_xor(x, 8);
+}
+__device__ __forceinline__ float xsum4(float x) {  // over lanes hl = 0..3 of a group
+  x += __shfl_xor(x, 1);
+  return x + __shfl_xor(x, 2);
+}
+__device__ __forceinline__ float xmaxg(float x) {  // over the 4 lane groups
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float xsumg(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(64 * kDW) void distill_kernel(DistillArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_dist[];
+  // K rows of the step: [hkv][64 keys][128] bf16, then the step's pooled
+  // keys [16][128] bf16, then per-wave scratch, then the dkbar sums
+  unsigned short* kls = (unsigned short*)smem_dist;
+  unsigned short* kbs = kls + (size_t)a.hkv * kStepKeys * 128;
+  float* scr = (float*)(kbs + kStepBlk * 128);  // [kDW][4 * 128] rotated queries / [kDW][32]
+  float* dks = scr + kDW * 4 * 128;            // [16][128] dkbar partial sums
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int hl = lane & 15, gq = lane >> 4;
+  const int ntiles = (a.n_q + kDW - 1) / kDW;
+  const int tile = ntiles - 1 - (int)(blockIdx.x % ntiles);  // longest rows first
+  const int b = (int)(blockIdx.x / ntiles);
+  const int t0 = tile * kDW;
+  const int t = t0 + wv;
+  const bool live = t < a.n_q;
+  const int64_t pos = a.q_pos0 + (live ? t : a.n_q - 1);
+  const int64_t nb = live ? (pos + 1) / 4 : 0;
+  const int t_last = min(a.n_q, t0 + kDW) - 1;
+  const int64_t pos_last = a.q_pos0 + t_last;
+  const int64_t nb_last = (pos_last + 1) / 4;
+  const int G = a.hq / a.hkv;
+  const float sl2 = a.scale * 1.4426950408889634f;
+  // the fields the lambdas below read, as locals (a kernel argument
+  // captured by reference would be kept in scratch memory)
+  const unsigned short* const kglob = a.k;
+  const unsigned short* const kbglob = a.kbar;
+  const int64_t n_cap = a.n_cap, nb_cap = a.nb_cap;
+  const int hkv = a.hkv, hq = a.hq, R = a.R;
+
+  // ---- prologue: Q^T operands (column hl = head), rotated indexer query
+  bf16x8 qb[4];
+  {
+    const unsigned short* qr = a.q + (((int64_t)b * a.n_q + (live ? t : 0)) * a.hq + hl) * 128;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (live && hl < a.hq) x = *(const u16x8*)(qr + 32 * cc + 8 * gq);
+      qb[cc] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+  float* qs = scr + wv * 4 * 128;  // q~ [4][128] of this wave's row
+  {
+    const int half = a.R / 2;
+    const unsigned short* qi = a.q_idx + ((int64_t)b * a.n_q + (live ? t : 0)) * 512;
+    for (int e = lane; e < 512; e += 64) {
+      const int d = e & 127;
+      const float x = live ? bf16_to_f32(qi[e]) : 0.f;
+      float val = x;
+      if (d < a.R) {
+        const int j = d < half ? d : d - half;
+        float c, s;
+        rope_cs(pos, j, a.R, a.log2_theta, &c, &s);
+        const float y = live ? bf16_to_f32(qi[(e & ~127) + (d < half ? d + half : d - half)]) : 0.f;
+        val = d < half ? (x * c - y * s) : (y * s + x * c);
+      }
+      qs[e] = val;
+    }
+  }
+  wave_sync();
+  // student B operands: column hl < 4 = indexer head, dims 32cc + 8gq; hi
+  // part, and a lo part for the rotated dims (cc < NLO)
+  bf16x8 ib[4], ibl[2];
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    u16x8 h = {0, 0, 0, 0, 0, 0, 0, 0}, lo = h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = hl < 4 ? qs[hl * 128 + 32 * cc + 8 * gq + e] : 0.f;
+      unsigned short hh, ll;
+      split_bf16(v, &hh, &ll);
+      h[e] = hh;
+      lo[e] = 32 * cc + 8 * gq + e < a.R ? ll : (unsigned short)0;
+    }
+    ib[cc] = __builtin_bit_cast(bf16x8, h);
+    if (cc < 2) ibl[cc] = __builtin_bit_cast(bf16x8, lo);
+  }
+  // the rotated query at this lane's dims (lane, lane + 64), all 4 heads
+  float qd[4][2];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    qd[h][0] = qs[h * 128 + lane];
+    qd[h][1] = qs[h * 128 + 64 + lane];
+  }
+  __syncthreads();  // scratch is reused below
+
+  // ---- a step's K rows (every KV head) and pooled keys into LDS ---------
+  const int nkv_ins = hkv * kStepKeys / 4;  // 1 KB instructions for K
+  auto stage = [&](int64_t k0, int64_t klim, bool with_kbar) {
+    const int nins = nkv_ins + (with_kbar ? kStepBlk / 4 : 0);
+    for (int ins = wv; ins < nins; ins += kDW) {
+      if (ins < nkv_ins) {
+        const int gg = ins / (kStepKeys / 4), kk = 4 * (ins % (kStepKeys / 4)) + (lane >> 4);
+        const int64_t key = k0 + kk;
+        const uint64_t row = key < klim ? (uint64_t)key : 0ull;
+        const unsigned short* src = kglob + (((int64_t)b * hkv + gg) * n_cap + row) * 128 +
+                                    8 * dswz(kk, lane & 15);
+        __builtin_amdgcn_global_load_lds((glb_void_t*)src,
+                                         (lds_void_t*)(kls + ((size_t)gg * kStepKeys + kk - (lane >> 4)) * 128),
+                                         16, 0, 0);
+      } else {
+        const int bb = 4 * (ins - nkv_ins) + (lane >> 4);
+        const int64_t blk = k0 / 4 + bb;
+        const uint64_t row = blk < nb_cap ? (uint64_t)blk : 0ull;
+        const unsigned short* src = kbglob + ((int64_t)b * nb_cap + row) * 128 +
+                                    8 * dswz(bb, lane & 15);
+        __builtin_amdgcn_global_load_lds((glb_void_t*)src,
+                                         (lds_void_t*)(kbs + (bb - (lane >> 4)) * 128), 16, 0, 0);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+  // teacher logits (log2 units) of key tile kt (16 keys) of the step for
+  // column hl: lane (hl, gq) holds keys 16kt + 4gq + i
+  auto teacher = [&](int kt, f32x4& out) {
+    const int gsel = hl < hq ? hl / G : 0;
+    out = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int gg = 0; gg < hkv; ++gg) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int kk = 16 * kt + hl;
+      const unsigned short* rowp = kls + ((size_t)gg * kStepKeys + kk) * 128;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const bf16x8 av = *(const bf16x8*)(rowp + 8 * dswz(kk, 4 * cc + gq));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[cc], acc, 0, 0, 0);
+      }
+      if (gg == gsel) out = acc;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] *= sl2;
+  };
+
+  // ---- pass 1: teacher log-sum-exp per head (base 2), keys 0 .. p -------
+  float lm = -INFINITY, ll = 0.f;
+  const int nstep1 = (int)((pos_last + 1 + kStepKeys - 1) / kStepKeys);
+  for (int st = 0; st < nstep1; ++st) {
+    const int64_t k0 = (int64_t)st * kStepKeys;
+    stage(k0, pos_last + 1, false);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      f32x4 s;
+      teacher(kt, s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t key = k0 + 16 * kt + 4 * gq + i;
+        if (!live || key > pos) continue;
+        const float x = s[i];
+        if (x > lm) {
+          ll = ll * exp2f(lm - x) + 1.f;
+          lm = x;
+        } else {
+          ll += exp2f(x - lm);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  float lse;
+  {
+    const float mm = xmaxg(lm);
+    lse = mm + log2f(xsumg(lm == -INFINITY ? 0.f : ll * exp2f(lm - mm)));
+  }
+
+  // per step: a_b and I_b of the step's 16 blocks; lane (hl, gq) ends with
+  // a and I of blocks 4gq + i (i < 4) and the sign bits of the 4 heads
+  float* wsc = scr + wv * 32;  // this wave's [16] a values, then [16] g values
+  auto block_terms = [&](int64_t k0, float* av, float* iv, uint64_t* sgn) {
+    // teacher: head-summed probabilities, maximum over the block's 4 keys
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      f32x4 s;
+      teacher(kt, s);
+      float mx = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t key = k0 + 16 * kt + 4 * gq + i;
+        const float pr = (live && hl < hq && key <= pos) ? exp2f(s[i] - lse) : 0.f;
+        mx = fmaxf(mx, xsum16(pr));
+      }
+      if (hl == 0) wsc[4 * kt + gq] = mx;  // block 4kt + gq
+    }
+    wave_sync();
+    // student: 16 blocks x 4 heads (columns hl < 4)
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int bb = hl;  // A row: block hl of the step
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const bf16x8 kv = *(const bf16x8*)(kbs + bb * 128 + 8 * dswz(bb, 4 * cc + gq));
+      if (cc < 2 && R > 0)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, ibl[cc], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, ib[cc], acc, 0, 0, 0);
+    }
+    // lane (hl, gq) holds <q~^hl, kbar> of blocks 4gq + i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sgn[i] = __ballot(hl < 4 && acc[i] > 0.f);
+      iv[i] = xsum4(hl < 4 ? relu(acc[i]) : 0.f);
+      av[i] = wsc[4 * gq + i];
+    }
+    wave_sync();
+  };
+
+  // ---- pass 2: normalisers and the loss ----------------------------------
+  const int nstep2 = (int)((nb_last + kStepBlk - 1) / kStepBlk);
+  float asum = 0.f, alog = 0.f, aI = 0.f, zm = -INFINITY, zl = 0.f;
+  for (int st = 0; st < nstep2; ++st) {
+    const int64_t k0 = (int64_t)st * kStepKeys;
+    stage(k0, pos_last + 1, true);
+    float av[4], iv[4];
+    uint64_t sgn[4];
+    block_terms(k0, av, iv, sgn);
+    if (hl == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t blk = (int64_t)st * kStepBlk + 4 * gq + i;
+        if (blk >= nb) continue;
+        asum += av[i];
+        alog += av[i] > 0.f ? av[i] * logf(av[i]) : 0.f;
+        aI += av[i] * iv[i];
+        if (iv[i] > zm) {
+          zl = zl * expf(zm - iv[i]) + 1.f;
+          zm = iv[i];
+        } else {
+          zl += expf(iv[i] - zm);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // combine the 4 lane groups (lanes hl = 0 carry the sums, others 0)
+  asum = xsumg(hl == 0 ? asum : 0.f);
+  alog = xsumg(hl == 0 ? alog : 0.f);
+  aI = xsumg(hl == 0 ? aI : 0.f);
+  float lnz;
+  {
+    const float zz = hl == 0 ? zm : -INFINITY;
+    const float mz = xmaxg(zz);
+    const float s = xsumg(hl == 0 && zm != -INFINITY ? zl * expf(zm - mz) : 0.f);
+    lnz = mz + logf(s);
+  }
+  const bool has = live && nb > 0;
+  if (live && lane == 0)
+    a.loss[(int64_t)b * a.n_q + t] =
+        has ? alog / asum - logf(asum) - aI / asum + lnz : 0.f;
+
+  // ---- pass 3: gradients -------------------------------------------------
+  float dq[4][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
+  const float inv_a = has ? 1.f / asum : 0.f;
+  for (int st = 0; st < nstep2; ++st) {
+    const int64_t k0 = (int64_t)st * kStepKeys;
+    for (int e = tid; e < kStepBlk * 128; e += 64 * kDW) dks[e] = 0.f;
+    stage(k0, pos_last + 1, true);
+    float av[4], iv[4];
+    uint64_t sgn[4];
+    block_terms(k0, av, iv, sgn);
+    // g of blocks 4gq + i, shared through the wave's scratch
+    if (hl == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t blk = (int64_t)st * kStepBlk + 4 * gq + i;
+        wsc[16 + 4 * gq + i] = (has && blk < nb) ? expf(iv[i] - lnz) - av[i] * inv_a : 0.f;
+      }
+    }
+    wave_sync();
+#pragma unroll
+    for (int bb = 0; bb < kStepBlk; ++bb) {
+      const float gb = wsc[16 + bb];
+      const int i = bb & 3, grp = bb >> 2;
+      const float k_lo = bf16_to_f32(kbs[bb * 128 + 8 * dswz(bb, lane >> 3) + (lane & 7)]);
+      const float k_hi = bf16_to_f32(kbs[bb * 128 + 8 * dswz(bb, 8 + (lane >> 3)) + (lane & 7)]);
+      float c0 = 0.f, c1 = 0.f;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const bool on = (sgn[i] >> (16 * grp + h)) & 1ull;
+        const float gh = on ? gb : 0.f;
+        dq[h][0] += gh * k_lo;
+        dq[h][1] += gh * k_hi;
+        c0 += gh * qd[h][0];
+        c1 += gh * qd[h][1];
+      }
+      atomicAdd(&dks[bb * 128 + lane], c0);
+      atomicAdd(&dks[bb * 128 + 64 + lane], c1);
+    }
+    __syncthreads();
+    // the workgroup's sums of this step's pooled-key gradients
+    for (int e = tid; e < kStepBlk * 128; e += 64 * kDW) {
+      const int64_t blk = (int64_t)st * kStepBlk + e / 128;
+      if (blk < nb_last && dks[e] != 0.f)
+        unsafeAtomicAdd(a.dkbar + ((int64_t)b * a.nb_cap + blk) * 128 + (e & 127), dks[e]);
+    }
+    __syncthreads();
+  }
+  // dq_idx: rotate back (angle -p) on the rotated dims; pair (j, j + R/2)
+  // lives in lanes j and j + R/2 (R <= 64)
+  if (live) {
+    const int half = a.R / 2;
+    float* out = a.dq_idx + ((int64_t)b * a.n_q + t) * 512;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      float v0 = dq[h][0];
+      const float partner = __shfl(v0, lane < a.R ? (lane < half ? lane + half : lane - half) : lane);
+      if (lane < a.R) {
+        const int j = lane < half ? lane : lane - half;
+        float c, s;
+        rope_cs(pos, j, a.R, a.log2_theta, &c, &s);
+        // inverse rotation: x' = x c + y s, y' = -x s + y c for the pair (x, y)
+        v0 = lane < half ? (v0 * c + partner * s) : (v0 * c - partner * s);
+      }
+      out[h * 128 + lane] = v0;
+      out[h * 128 + 64 + lane] = dq[h][1];
+    }
+  }
+}
+
+size_t distill_lds(int hkv) {
+  return (size_t)hkv * kStepKeys * 128 * 2 + kStepBlk * 128 * 2 + kDW * 4 * 128 * 4 +
+         kStepBlk * 128 * 4;
+}
+
+hipError_t launch_distill(const DistillArgs& a, hipStream_t st) {
+  const int ntiles = (a.n_q + kDW - 1) / kDW;
+  const int64_t grid = (int64_t)ntiles * a.B;
+  if (grid == 0) return hipSuccess;
+  const size_t lds = distill_lds(a.hkv);
+  hipError_t e = hipFuncSetAttribute((const void*)distill_kernel,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(distill_kernel, dim3((unsigned)grid), dim3(64 * kDW), lds, st, a);
+  return hipGetLastError();
+}
+
+// Pooling backward: dk_idx rows of blocks [b0, b1) from dkbar: each of the
+// block's 4 keys gets dkbar rotated back (angle -(4b + 3)) divided by 4.
+__global__ __launch_bounds__(256) void pool_backward_kernel(const float* dkbar, int64_t nb_cap,
+                                                            float* dk, int64_t n_cap, int B,
+                                                            int64_t b0, int64_t nblk, int r,
+                                                            int R, double log2_theta) {
+  const int lane = threadIdx.x & 63;
+  const int64_t job = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (job >= (int64_t)B * nblk) return;
+  const int64_t b = job / nblk, j = b0 + job % nblk;
+  const float* src = dkbar + (b * nb_cap + j) * 128;
+  const int half = R / 2;
+  float v[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = lane + 64 * i;
+    float x = src[c];
+    if (c < R) {
+      const int jj = c < half ? c : c - half;
+      float cs, sn;
+      rope_cs((j + 1) * r - 1, jj, R, log2_theta, &cs, &sn);
+      const float y = src[c < half ? c + half : c - half];
+      x = c < half ? (x * cs + y * sn) : (x * cs - y * sn);
+    }
+    v[i] = x / (float)r;
+  }
+  for (int t = 0; t < r; ++t) {
+    float* dst = dk + (b * n_cap + j * r + t) * 128;
+    dst[lane] = v[0];
+    dst[lane + 64] = v[1];
+  }
+}
+
+hipError_t launch_pool_backward(const float* dkbar, int64_t nb_cap, float* dk, int64_t n_cap,
+                                int B, int64_t b0, int64_t b1, int r, int R, double log2_theta,
+                                hipStream_t st) {
+  const int64_t jobs = (int64_t)B * (b1 - b0);
+  if (jobs == 0) return hipSuccess;
+  hipLaunchKernelGGL(pool_backward_kernel, dim3((unsigned)((jobs + 3) / 4)), dim3(256), 0, st,
+                     dkbar, nb_cap, dk, n_cap, B, b0, b1 - b0, r, R, log2_theta);
+  return hipGetLastError();
+}
+
+}  // namespace qsa

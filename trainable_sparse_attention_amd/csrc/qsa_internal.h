@@ -124,6 +124,29 @@ hipError_t launch_attn_prefill(qsa_dtype dt, const AttnArgs& a, hipStream_t st);
 // merge nsplit partials per (sequence, token, KV head) into a.out
 hipError_t launch_attn_combine(qsa_dtype dt, const AttnArgs& a, int nsplit, const float* part,
                                hipStream_t st);
+// sparse attention backward (bf16 inputs): dq written, dk / dv accumulated
+hipError_t launch_attn_backward(const AttnArgs& a, const void* dout, float* dq, float* dk,
+                                float* dv, hipStream_t st);
+// indexer distillation (r = 4, bf16): loss and dq_idx written, dkbar added to
+struct DistillArgs {
+  const unsigned short* q;      // [B][n_q][hq][128]
+  const unsigned short* k;      // [B][hkv][n_cap][128]
+  const unsigned short* q_idx;  // [B][n_q][4][128]
+  const unsigned short* kbar;   // [B][nb_cap][128]
+  float* loss;                  // [B][n_q]
+  float* dq_idx;                // [B][n_q][4][128]
+  float* dkbar;                 // [B][nb_cap][128], added to
+  int64_t n_cap, nb_cap, q_pos0;
+  int B, n_q, hq, hkv, R;
+  float scale;
+  double log2_theta;
+};
+size_t distill_lds(int hkv);
+hipError_t launch_distill(const DistillArgs& a, hipStream_t st);
+// pooling backward: dk rows of blocks [b0, b1) written from dkbar
+hipError_t launch_pool_backward(const float* dkbar, int64_t nb_cap, float* dk, int64_t n_cap,
+                                int B, int64_t b0, int64_t b1, int r, int R, double log2_theta,
+                                hipStream_t st);
 // dense causal GQA attention (bf16; hq/hkv divides 16)
 hipError_t launch_dense_prefill(const AttnArgs& a, hipStream_t st);
 size_t dense_decode_workspace(int B, int n_q, int hkv, int64_t n_cap);

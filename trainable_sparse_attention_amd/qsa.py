@@ -22,7 +22,9 @@ EXPORTS = ["qsa_default_params", "qsa_k_blocks", "qsa_status_str", "qsa_last_err
            "qsa_index_topk_workspace",
            "qsa_sparse_attn_prefill", "qsa_sparse_attn_decode",
            "qsa_sparse_attn_decode_workspace", "qsa_sparse_attn_decode_shared",
-           "qsa_sparse_attn_decode_noalloc", "qsa_dense_attn_prefill",
+           "qsa_sparse_attn_decode_noalloc", "qsa_sparse_attn_backward", "qsa_index_distill",
+           "qsa_pool_keys_backward",
+           "qsa_dense_attn_prefill",
            "qsa_dense_attn_decode", "qsa_dense_attn_decode_workspace",
            "qsa_probe_gather"]
 
@@ -85,6 +87,14 @@ def lib():
         L.qsa_sparse_attn_decode_noalloc.argtypes = [PP, ctypes.c_int, P, P, P, I64, P, P, P,
                                                      I32, I32, I32, I32, I32, F, P, P]
         L.qsa_sparse_attn_decode_noalloc.restype = ctypes.c_int
+        L.qsa_sparse_attn_backward.argtypes = [PP, ctypes.c_int, P, P, P, I64, P, P, P, P, I32,
+                                               I32, I64, I32, I32, I32, F, P, P, P, P]
+        L.qsa_sparse_attn_backward.restype = ctypes.c_int
+        L.qsa_index_distill.argtypes = [PP, ctypes.c_int, P, P, I64, P, P, I64, I32, I32, I64, I32,
+                                        I32, I32, F, P, P, P, P]
+        L.qsa_index_distill.restype = ctypes.c_int
+        L.qsa_pool_keys_backward.argtypes = [PP, P, I64, P, I64, I32, I64, I64, P]
+        L.qsa_pool_keys_backward.restype = ctypes.c_int
         L.qsa_dense_attn_prefill.argtypes = [ctypes.c_int, P, P, P, I64, I32, I32, I64, I32, I32,
                                              I32, F, P, P]
         L.qsa_dense_attn_prefill.restype = ctypes.c_int
@@ -214,6 +224,39 @@ def qsa_sparse_attn_decode_noalloc(p, q, k_cache, v_cache, seq_len, idx, cnt, ou
                                                 _ptr(k_cache), _ptr(v_cache), n_cap,
                                                 _ptr(seq_len), _ptr(idx), _ptr(cnt), B, n_q, hq,
                                                 hkv, d, scale, _ptr(out), _stream(stream)))
+
+
+def qsa_sparse_attn_backward(p, q, k, v, idx, cnt, out, dout, dq, dk, dv, q_pos0=0, scale=0.0,
+                             stream=None):
+    """Gradients of the sparse attention (bf16 inputs): dq [B][n_q][hq][d]
+    float32 written; dk, dv [B][hkv][n_cap][d] float32 added to."""
+    B, n_q, hq, d = q.shape
+    hkv, n_cap = k.shape[1], k.shape[2]
+    _check(lib().qsa_sparse_attn_backward(ctypes.byref(p), dtype_code(q), _ptr(q), _ptr(k),
+                                          _ptr(v), n_cap, _ptr(idx), _ptr(cnt), _ptr(out),
+                                          _ptr(dout), B, n_q, q_pos0, hq, hkv, d, scale, _ptr(dq),
+                                          _ptr(dk), _ptr(dv), _stream(stream)))
+
+
+def qsa_index_distill(p, q, k, q_idx, kbar, loss, dq_idx, dkbar, q_pos0=0, scale=0.0,
+                      stream=None):
+    """Stage-1 distillation of the indexer: loss [B][n_q] and dq_idx
+    [B][n_q][4][128] written, dkbar [B][nb_cap][128] added to (float32)."""
+    B, n_q, hq, d = q.shape
+    hkv, n_cap = k.shape[1], k.shape[2]
+    _check(lib().qsa_index_distill(ctypes.byref(p), dtype_code(q), _ptr(q), _ptr(k), n_cap,
+                                   _ptr(q_idx), _ptr(kbar), kbar.shape[1], B, n_q, q_pos0, hq, hkv,
+                                   d, scale, _ptr(loss), _ptr(dq_idx), _ptr(dkbar),
+                                   _stream(stream)))
+
+
+def qsa_pool_keys_backward(p, dkbar, dk_idx, block_begin, block_end, stream=None):
+    """dk_idx [B][n_cap][128] rows of blocks [begin, end) from dkbar
+    [B][nb_cap][128] (float32)."""
+    B = dkbar.shape[0]
+    _check(lib().qsa_pool_keys_backward(ctypes.byref(p), _ptr(dkbar), dkbar.shape[1],
+                                        _ptr(dk_idx), dk_idx.shape[1], B, block_begin, block_end,
+                                        _stream(stream)))
 
 
 def qsa_dense_attn_prefill(q, k, v, out, q_pos0=0, scale=0.0, stream=None):
