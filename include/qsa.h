@@ -38,7 +38,8 @@
  *     in the caches).  Block b is visible to position p iff (b+1)r-1 <= p.
  *   - Inputs must be finite; NaN or Inf give undefined selections.
  *   - Results are deterministic: identical inputs give identical bits.
- *   - Supported shapes: r in {1, 2, 4, 8, 16}, h_idx = 4, d_idx = 128, rope_dims even and
+ *   - Supported shapes: r in {1, 2, 4, 8, 16}, h_idx in {1, 2, 4} (q_idx
+ *     then holds h_idx heads per token), d_idx = 128, rope_dims even and
  *     <= 128, K >= r, head dim d = 128, hq % hkv == 0, hq / hkv <= 16;
  *     k_B = ceil(K/r) <= 3072 for qsa_index_topk over more than 4 query rows
  *     per sequence and <= 4096 for its decode form (at most 4 new tokens);
@@ -138,7 +139,8 @@ qsa_status qsa_pool_keys_rmsnorm(const qsa_params* p, qsa_dtype dtype, const voi
  * under the total order (score descending, block id ascending), written as
  * ascending block ids, padded with -1.  The score matrix is never stored.
  *
- *   q_idx : [B][n_q][h_idx][d_idx]  indexer queries, NOT rotated
+ *   q_idx : [B][n_q][h_idx][d_idx]  indexer queries, NOT rotated (h_idx
+ *                                   is 1, 2 or 4)
  *   kbar  : [B][nb_cap][d_idx]      pooled keys from qsa_pool_keys
  *   d_seq_len : NULL (prefill: positions q_pos0 + t) or device int32 [B]
  *               (decode: positions d_seq_len[b] - n_q + t)

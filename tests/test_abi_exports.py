@@ -105,6 +105,16 @@ def test_host_validation_of_built_limits():
     dec = qsa.params(K=4 * 4097)           # decode form: k_B = 4097
     _expect(lib.qsa_index_topk(ctypes.byref(dec), 1, fake, fake, 1 << 16, 2, 1, 0, fake, fake,
                                fake, fake, 1 << 40, None), 4, lib)
+    # indexer head counts: 1, 2 and 4 are built (absent heads are zero
+    # queries), 3 and 8 are not
+    for h, want in ((3, 4), (8, 4)):
+        ph = qsa.params(h_idx=h)
+        _expect(lib.qsa_index_topk(ctypes.byref(ph), 1, fake, fake, 1 << 16, 1, 4096, 0, None,
+                                   fake, fake, fake, 1 << 40, None), want, lib)
+    for h in (1, 2):
+        ph = qsa.params(h_idx=h)        # passes to the workspace check
+        _expect(lib.qsa_index_topk(ctypes.byref(ph), 1, fake, fake, 1 << 16, 1, 4096, 0, None,
+                                   fake, fake, None, 0, None), 5, lib)
     p = qsa.params()
     P = ctypes.byref(p)
     cap = (1 << 24) + 4

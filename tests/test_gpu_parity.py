@@ -461,6 +461,53 @@ def test_block_size_variants_decode(r, n_q, lens):
         assert rel_err(s_out[b], os_) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("h,dtype,n", [(1, "bf16", 9000), (2, "bf16", 9000), (2, "fp32", 3000),
+                                        (1, "fp32", 3000)])
+def test_indexer_head_counts_prefill(h, dtype, n):
+    """Indexers with fewer query heads ([hub] "Key ideas": the ReLU-sum runs
+    over the indexer's own heads): selections against the oracle with h heads."""
+    say("indexer heads h=%d %s n=%d" % (h, dtype, n))
+    K = 2048
+    p = qsa.params(K=K, h_idx=h)
+    d = inputs.small(B=2, n=n, hq=4, hkv=1, dtype=dtype, K=K, seed=500 + h, planted=0)
+    q_idx = np.ascontiguousarray(d["q_idx"][:, :, :h])
+    kbar = torch.empty((2, n // 4, 128), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32,
+                       device="cuda")
+    qsa.qsa_pool_keys(p, to_dev(d["k_idx"]), kbar, 0, n // 4)
+    idx, cnt = _index_gpu(p, to_dev(q_idx), kbar)
+    torch.cuda.synchronize()
+    kbar_h, g_idx, g_cnt = to_host(kbar), to_host(idx), to_host(cnt)
+    rows = _transition_rows(n, qsa.k_blocks(p), 4)
+    for b in range(2):
+        o_idx, o_cnt = oracle.index_rows(q_idx[b], kbar_h[b], rows, K=K)
+        gi, gc = g_idx[b][rows], g_cnt[b][rows]
+        assert np.array_equal(gc, o_cnt), "counts differ"
+        sc = oracle.score_rows(q_idx[b], kbar_h[b], rows)
+        check_sets(gi, gc, o_idx, o_cnt, sc)
+
+
+@pytest.mark.parametrize("h,n_q", [(1, 1), (2, 4)])
+def test_indexer_head_counts_decode(h, n_q):
+    say("indexer heads decode h=%d n_q=%d" % (h, n_q))
+    lens = [9000, 4099, 30001]
+    n = max(lens)
+    K = 2048
+    p = qsa.params(K=K, h_idx=h)
+    d = inputs.small(B=3, n=n, hq=4, hkv=1, dtype="bf16", K=K, seed=510 + h, planted=0)
+    kbar = torch.empty((3, n // 4, 128), dtype=torch.bfloat16, device="cuda")
+    qsa.qsa_pool_keys(p, to_dev(d["k_idx"]), kbar, 0, n // 4)
+    q_idx = np.ascontiguousarray(np.stack([d["q_idx"][b, L - n_q:L, :h] for b, L in enumerate(lens)]))
+    seq_len = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    idx, cnt = _index_gpu(p, to_dev(q_idx), kbar, seq_len=seq_len)
+    torch.cuda.synchronize()
+    kbar_h, g_idx, g_cnt = to_host(kbar), to_host(idx), to_host(cnt)
+    for b, L in enumerate(lens):
+        pos = np.arange(L - n_q, L)
+        o_idx, o_cnt = oracle.index_at(q_idx[b], kbar_h[b], pos, K=K)
+        sc = oracle.score_at(q_idx[b], kbar_h[b], pos)
+        check_sets(g_idx[b], g_cnt[b], o_idx, o_cnt, sc)
+
+
 # ---- dense causal GQA attention (QSA with every block selected; the
 # pages' dense baseline, [glide] "QSA Ablations and Efficiency", Figure 6) ----
 

@@ -39,7 +39,8 @@ static qsa_status check_params(const qsa_params* p) {
   if (p->r != 1 && p->r != 2 && p->r != 4 && p->r != 8 && p->r != 16)
     return fail(QSA_ERR_UNSUPPORTED, "r=%d: built for r in {1, 2, 4, 8, 16}", p->r);
   if (p->K < p->r) return fail(QSA_ERR_SHAPE, "K=%d must be >= r=%d", p->K, p->r);
-  if (p->h_idx != 4) return fail(QSA_ERR_UNSUPPORTED, "h_idx=%d: only 4 indexer heads", p->h_idx);
+  if (p->h_idx != 1 && p->h_idx != 2 && p->h_idx != 4)
+    return fail(QSA_ERR_UNSUPPORTED, "h_idx=%d: built for 1, 2 or 4 indexer heads", p->h_idx);
   if (p->d_idx != 128) return fail(QSA_ERR_UNSUPPORTED, "d_idx=%d: only 128", p->d_idx);
   if (p->rope_dims < 0 || p->rope_dims > 128 || (p->rope_dims & 1))
     return fail(QSA_ERR_UNSUPPORTED, "rope_dims=%d must be even and <= 128", p->rope_dims);
@@ -184,6 +185,7 @@ qsa_status qsa_index_topk(const qsa_params* p, qsa_dtype dtype, const void* q_id
   a.kB = kB;
   a.r = p->r;
   a.R = p->rope_dims;
+  a.h = p->h_idx;
   a.log2_theta = log2((double)p->rope_theta);
   hipError_t e = dec ? launch_index_decode(dtype, a, workspace, (hipStream_t)stream)
                      : launch_index_prefill(dtype, a, workspace, num_cus(), (hipStream_t)stream);
@@ -407,6 +409,7 @@ qsa_status qsa_index_distill(const qsa_params* p, qsa_dtype dtype, const void* q
   if (s) return s;
   if ((s = check_dtype(dtype))) return s;
   if (dtype != QSA_BF16) return fail(QSA_ERR_UNSUPPORTED, "distillation is built for bf16");
+  if (p->h_idx != 4) return fail(QSA_ERR_UNSUPPORTED, "distillation is built for 4 indexer heads");
   if (p->r != 4) return fail(QSA_ERR_UNSUPPORTED, "distillation is built for r = 4");
   if (p->rope_dims > 64) return fail(QSA_ERR_UNSUPPORTED, "distillation: rope_dims <= 64");
   if (!q || !k || !q_idx || !kbar || !loss || !dq_idx || !dkbar)

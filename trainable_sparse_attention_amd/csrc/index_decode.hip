@@ -118,14 +118,15 @@ __global__ __launch_bounds__(256) void index_decode_prep(IndexArgs a, DecodeWs w
   const int half = a.R / 2;
   const int64_t pos = dec_pos(a, b, t);
   // the query values are loaded first; the angles are formed while they fly
-  const T* qr0 = (const T*)a.q_idx + (int64_t)row * 4 * 128;
+  const T* qr0 = (const T*)a.q_idx + (int64_t)row * a.h * 128;
   float xv[2], yv[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {  // elements tid and tid + 256 of the 4 x 128
     const int e = tid + 256 * k, hh = e >> 7, d = e & 127;
     const T* qr = qr0 + hh * 128;
-    xv[k] = Elt<T>::ld(qr, d);
-    yv[k] = d < a.R ? Elt<T>::ld(qr, d < half ? d + half : d - half) : 0.f;
+    // head slots at or above h are zero queries
+    xv[k] = hh < a.h ? Elt<T>::ld(qr, d) : 0.f;
+    yv[k] = hh < a.h && d < a.R ? Elt<T>::ld(qr, d < half ? d + half : d - half) : 0.f;
   }
   for (int j = tid; j < half; j += 256) {
     float c, s;

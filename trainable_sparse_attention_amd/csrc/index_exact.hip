@@ -161,8 +161,8 @@ __global__ __launch_bounds__(512, 1) void index_exact_kernel(IndexArgs a, uint64
             const int ql = kRPW * wv + 8 * rt + (m >> 2), hh = m & 3;
             const int t = row0 + ql;
             float val = 0.f;
-            if (t < a.n_q) {
-              const T* qr = qsrc + (((int64_t)b * a.n_q + t) * 4 + hh) * 128;
+            if (t < a.n_q && hh < a.h) {
+              const T* qr = qsrc + (((int64_t)b * a.n_q + t) * a.h + hh) * 128;
               const float x = Elt<T>::ld(qr, d);
               if (d < a.R) {
                 const int j = d < half ? d : d - half;

@@ -135,7 +135,8 @@ __global__ __launch_bounds__(1024, 1) void index_scan_kernel(IndexArgs a, PipeWs
     // run; four queries at a time go to LDS (load j of a lane brings 16
     // bytes of query j, all four in flight together; absent queries read as
     // zeros) for the rotation, which pairs dims across lanes
-    const uint4* qw = (const uint4*)a.q_idx + ((int64_t)G.b * a.n_q + G.row0 + 8 * wv) * 64;
+    // (with h < 4 indexer heads a query is h * 16 uint4; slots h .. 3 are zero)
+    const uint4* qw = (const uint4*)a.q_idx + ((int64_t)G.b * a.n_q + G.row0 + 8 * wv) * (16 * a.h);
     uint4* rawq = (uint4*)(smem + 2 * kStageBytes + 32768) + wv * 256;
 #pragma unroll 1
     for (int hf = 0; hf < 4; ++hf) {
@@ -144,7 +145,9 @@ __global__ __launch_bounds__(1024, 1) void index_scan_kernel(IndexArgs a, PipeWs
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int ql = 2 * hf + j;
-          rq[j] = G.row0 + 8 * wv + ql < a.n_q ? qw[ql * 64 + lane] : uint4{0u, 0u, 0u, 0u};
+          rq[j] = (G.row0 + 8 * wv + ql < a.n_q && (lane >> 4) < a.h)
+                      ? qw[ql * (16 * a.h) + lane]
+                      : uint4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) rawq[j * 64 + lane] = rq[j];

@@ -84,6 +84,9 @@ struct IndexArgs {
   int32_t* idx;
   int32_t* cnt;
   int kB, r, R;
+  // indexer query heads (1, 2 or 4); the kernels score 4 head slots, the
+  // ones at or above h read as zero queries (ReLU(0) adds nothing)
+  int h;
   double log2_theta;
 };
 

@@ -167,8 +167,10 @@ def qsa_index_topk_workspace(p, dtype, B, n_q, nb_cap, decode):
 
 
 def qsa_index_topk(p, q_idx, kbar, idx, cnt, workspace, q_pos0=0, seq_len=None, stream=None):
-    """q_idx [B][n_q][4][128], kbar [B][nb_cap][128] -> idx [B][n_q][k_B], cnt [B][n_q]."""
+    """q_idx [B][n_q][h_idx][128], kbar [B][nb_cap][128] -> idx [B][n_q][k_B], cnt [B][n_q]."""
     B, n_q = q_idx.shape[0], q_idx.shape[1]
+    if q_idx.dim() != 4 or q_idx.shape[2] != p.h_idx:
+        raise ValueError("q_idx must be [B][n_q][h_idx=%d][d]" % p.h_idx)
     _check(lib().qsa_index_topk(ctypes.byref(p), dtype_code(q_idx), _ptr(q_idx), _ptr(kbar),
                                 kbar.shape[1], B, n_q, q_pos0, _ptr(seq_len), _ptr(idx),
                                 _ptr(cnt), _ptr(workspace),
