@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense GQA comparison (chunked prefill and decode)")
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--no-train", action="store_true",
+                    help="skip the training kernels (distillation, backward)")
     ap.add_argument("--cpu-rows", type=int, default=16384,
                     help="uniformly spaced prefill rows the CPU oracle computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -71,10 +73,11 @@ def log(*a):
 
 
 class ClockSampler:
-    """Samples the graphics clock of device 0 (amdsmi metrics table, mean
-    over the XCDs) every few ms on a host thread while the timed steps run;
-    reports min / median / max MHz.
-    Informative only: any failure is recorded, not raised."""
+    """Samples the graphics clock of device 0 (amdsmi clock info) every few
+    ms on a host thread while the timed steps run; reports min / median / max
+    MHz of the plausible readings.  Informative only: any failure is
+    recorded, not raised.  The clocks the kernels hold under their own load
+    are read from GRBM counters in separate profiler runs."""
 
     def __init__(self):
         self.vals, self.err, self._stop = [], None, None
@@ -96,14 +99,12 @@ class ClockSampler:
         def run():
             while not self._stop.is_set():
                 try:
-                    # per-XCD current graphics clocks from the metrics table
-                    m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
-                    xs = [x for x in (m.get("current_gfxclks") or [])
-                          if isinstance(x, (int, float)) and 0 < x < 10000]
-                    if not xs and isinstance(m.get("current_gfxclk"), (int, float)):
-                        xs = [m["current_gfxclk"]]
-                    if xs:
-                        self.vals.append(sum(xs) / len(xs))
+                    # the SMU's current graphics clock; readings outside a
+                    # plausible range (idle or other clock domains) are dropped
+                    c = self._smi.amdsmi_get_clock_info(self._h, self._smi.AmdSmiClkType.GFX)
+                    x = c.get("clk")
+                    if isinstance(x, (int, float)) and 500 <= x <= 3000:
+                        self.vals.append(x)
                 except Exception as e:
                     self.err = str(e)[:120]
                     return
@@ -413,6 +414,92 @@ def bench_dense_comparison(args, torch, qsa, inputs, flush):
                                    PEAK_HBM_GBS}}
 
 
+def bench_training(args, torch, qsa, inputs, flush):
+    """The training kernels at a training context length ([hub] "Key ideas",
+    native-trainability bullet): stage-1 indexer distillation (loss and
+    gradients against the dense teacher), the pooling backward that carries
+    the pooled-key gradient to the raw indexer keys, and the stage-2
+    sparse-attention backward.  The forward (pool, select, attend) runs once,
+    untimed; the gradient buffers the kernels add into are cleared inside
+    the timed step."""
+    d = inputs.make("train_32k", seed=8, backend="torch")
+    p = qsa.params()
+    B, n, hq, hkv = d["B"], d["n"], d["hq"], d["hkv"]
+    kB = qsa.k_blocks(p)
+    nb = n // p.r
+    dev = d["q"].device
+    stream = torch.cuda.current_stream()
+    kbar = torch.empty((B, nb, 128), dtype=torch.bfloat16, device=dev)
+    qsa.qsa_pool_keys(p, d["k_idx"], kbar, 0, nb, stream)
+    idx = torch.empty((B, n, kB), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, n), dtype=torch.int32, device=dev)
+    ws = qsa.workspace(qsa.qsa_index_topk_workspace(p, qsa.QSA_BF16, B, n, nb, False))
+    qsa.qsa_index_topk(p, d["q_idx"], kbar, idx, cnt, ws, 0, None, stream)
+    out = torch.empty_like(d["q"])
+    qsa.qsa_sparse_attn_prefill(p, d["q"], d["k"], d["v"], idx, cnt, out, 0, 0.0, stream)
+    g = torch.Generator(device=dev)
+    g.manual_seed(9)
+    dout = (torch.randn(out.shape, generator=g, device=dev) * 0.1).to(torch.bfloat16)
+    loss = torch.empty((B, n), dtype=torch.float32, device=dev)
+    dq_idx = torch.empty((B, n, 4, 128), dtype=torch.float32, device=dev)
+    dkbar = torch.empty((B, nb, 128), dtype=torch.float32, device=dev)
+    dk_idx = torch.empty((B, n, 128), dtype=torch.float32, device=dev)
+    dq = torch.empty((B, n, hq, 128), dtype=torch.float32, device=dev)
+    dk = torch.empty((B, hkv, n, 128), dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    stages = [lambda: (dkbar.zero_(), dk.zero_(), dv.zero_()),
+              lambda: qsa.qsa_index_distill(p, d["q"], d["k"], d["q_idx"], kbar, loss, dq_idx,
+                                            dkbar, 0, 0.0, stream),
+              lambda: qsa.qsa_pool_keys_backward(p, dkbar, dk_idx, 0, nb, stream),
+              lambda: qsa.qsa_sparse_attn_backward(p, d["q"], d["k"], d["v"], idx, cnt, out,
+                                                   dout, dq, dk, dv, 0, 0.0, stream)]
+    for _ in range(max(1, args.warmup)):
+        for f in stages:
+            f()
+    K = max(1, min(args.steps, 3))
+    ms, _ = time_steps(torch, stream, stages, K, flush)
+    # each call timed on its own (events between calls inside one step can
+    # be stamped early after a long kernel); the gradient buffers are
+    # cleared, untimed, before every call that adds into them
+    st = [time_steps(torch, stream, [stages[0]], K, flush)[0]]
+    for i in (1, 2, 3):
+        t = 0.0
+        for _ in range(K):
+            stages[0]()
+            t += time_steps(torch, stream, [stages[i]], 1, flush)[0]
+        st.append(t / K)
+    c = cnt.to(torch.int64)
+    pos = torch.arange(n, device=dev, dtype=torch.int64)
+    slots = int(c.sum().item()) * p.r + int(((pos + 1) % p.r).sum().item()) * B
+    pairs = sum_nb(n, p.r) * B
+    causal = B * n * (n + 1) // 2
+    # algorithmic work: the teacher's logits once (2 d flops per head and
+    # key), the student's scores and its two gradients (3 x 2 d per indexer
+    # head and block); the backward's five products per head and gathered
+    # key (logits recomputed, dP, dV, dQ, dK)
+    distill_flop = 2.0 * 128 * hq * causal + 3 * 2.0 * 128 * 4 * pairs
+    bwd_flop = 10.0 * 128 * hq * slots
+    pool_bwd_bytes = B * (nb * 128 * 4 + n * 128 * 4)
+    res = {"workload": inputs.describe("train_32k"), "ms_per_step": ms,
+           "stage_ms": {"clear_gradients": st[0], "index_distill": st[1],
+                        "pool_keys_backward": st[2], "sparse_attn_backward": st[3]},
+           "index_distill": {"TFLOP/s": distill_flop / (st[1] * 1e-3) / 1e12,
+                             "frac_mfma": distill_flop / (st[1] * 1e-3) / 1e12 /
+                             PEAK_BF16_TFLOPS, "flop": distill_flop},
+           "sparse_attn_backward": {"TFLOP/s": bwd_flop / (st[3] * 1e-3) / 1e12,
+                                    "frac_mfma": bwd_flop / (st[3] * 1e-3) / 1e12 /
+                                    PEAK_BF16_TFLOPS, "flop": bwd_flop, "sum_T": slots},
+           "pool_keys_backward": {"GB/s": pool_bwd_bytes / (st[2] * 1e-3) / 1e9,
+                                  "frac_hbm": pool_bwd_bytes / (st[2] * 1e-3) / 1e9 /
+                                  PEAK_HBM_GBS},
+           "mean_loss": float(loss.mean().item())}
+    log("training kernels %s: %.3f ms/step (clear %.3f, distill %.3f = %.1f TFLOP/s, pool bwd "
+        "%.4f, attn bwd %.3f = %.1f TFLOP/s)" % ("train_32k", ms, st[0], st[1],
+                                                 res["index_distill"]["TFLOP/s"], st[2], st[3],
+                                                 res["sparse_attn_backward"]["TFLOP/s"]))
+    return res
+
+
 def decode_record(inputs, dec, steps):
     return {
         "value": dec["tok_s"], "unit": "tokens/s", "ms_per_step": dec["ms"],
@@ -512,6 +599,11 @@ def main():
             decs.append(dec)
             torch.cuda.empty_cache()
 
+    train = None
+    if not args.no_train:
+        train = bench_training(args, torch, qsa, inputs, flush)
+        torch.cuda.empty_cache()
+
     cmp_ = None
     if not args.no_dense:
         cmp_ = bench_dense_comparison(args, torch, qsa, inputs, flush)
@@ -581,6 +673,8 @@ def main():
     }
     if cmp_ is not None:
         line["qsa_vs_dense"] = cmp_
+    if train is not None:
+        line["training"] = train
     if decs:
         line["decode"] = decode_record(inputs, decs[0], args.decode_steps)
         if len(decs) > 1:

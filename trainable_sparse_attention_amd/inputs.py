@@ -50,6 +50,10 @@ CONFIGS = {
                         planted=1024),
     "decode_4x1m_next4": dict(mode="decode", B=4, n=1048576, n_new=4, hq=16, hkv=2,
                               dtype="bf16", planted=1024),
+    # one training step's kernels at a training context length: indexer
+    # distillation (dense teacher) and the sparse-attention backward
+    "train_32k": dict(mode="prefill", B=1, n=32768, hq=16, hkv=2, dtype="bf16", planted=0,
+                      train=True),
 }
 
 
@@ -59,6 +63,10 @@ def describe(name):
     dt = "bf16" if c["dtype"] == "bf16" else "float32"
     heads = "indexer 4x128 query heads + 1x128 key head, attention %d q / %d kv heads, d=128" % (
         c["hq"], c["hkv"])
+    if c.get("train"):
+        return "QSA training kernels (indexer distillation against the dense teacher, " \
+               "pooling backward, sparse-attention backward), batch %d, n=%d tokens, K=2048, " \
+               "r=4, %s, %s" % (c["B"], c["n"], heads, dt)
     if c["mode"] == "prefill":
         return "QSA prefill, batch %d, n=%d tokens, K=2048, r=4, %s, %s" % (c["B"], c["n"],
                                                                          heads, dt)
