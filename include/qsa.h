@@ -278,15 +278,28 @@ qsa_status qsa_sparse_attn_decode_noalloc(const qsa_params* p, qsa_dtype dtype, 
  *   dq : [B][n_q][hq][d] float32, written;
  *   dk, dv : [B][hkv][n_cap][d] float32, ADDED to (the caller clears them;
  *            rows attended by no query are left untouched)
- * Errors as for qsa_sparse_attn_prefill; float32 inputs ->
- * QSA_ERR_UNSUPPORTED.
+ *   workspace : device scratch of qsa_sparse_attn_backward_workspace(...)
+ *               bytes (per-row log-sum-exp and <dout, out>, and the
+ *               selection transposed to per-block lists of rows, so that
+ *               each key row's gradient is summed by one owner: no float
+ *               atomics; the sums run in ascending row order, so the result
+ *               is deterministic while no block is selected by more than
+ *               16384 rows of one call)
+ * Errors as for qsa_sparse_attn_prefill; float32 inputs or n_q * k_B above
+ * 2^31 -> QSA_ERR_UNSUPPORTED; workspace too small -> QSA_ERR_WORKSPACE.
  */
 qsa_status qsa_sparse_attn_backward(const qsa_params* p, qsa_dtype dtype, const void* q,
                                     const void* k, const void* v, int64_t n_cap,
                                     const int32_t* idx, const int32_t* cnt, const void* out,
                                     const void* dout, int32_t B, int32_t n_q, int64_t q_pos0,
                                     int32_t hq, int32_t hkv, int32_t d, float scale, float* dq,
-                                    float* dk, float* dv, void* stream);
+                                    float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/* Workspace bytes qsa_sparse_attn_backward needs for these sizes (0 for
+ * invalid parameters). */
+size_t qsa_sparse_attn_backward_workspace(const qsa_params* p, int32_t B, int32_t n_q,
+                                          int64_t q_pos0, int32_t hq);
 
 /*
  * qsa_index_distill -- stage-1 indexer distillation ([hub] "Key ideas",

@@ -59,10 +59,19 @@ def test_sparse_attn_backward(r, n, K, q_pos0):
     dq = torch.empty((B, n_q, hq, 128), dtype=torch.float32, device="cuda")
     dk = torch.zeros((B, hkv, n, 128), dtype=torch.float32, device="cuda")
     dv = torch.zeros_like(dk)
-    qsa.qsa_sparse_attn_backward(p, qq, t["k"], t["v"], idx, cnt, out, dout, dq, dk, dv, q_pos0)
+    wsb = qsa.workspace(qsa.qsa_sparse_attn_backward_workspace(p, B, n_q, q_pos0, hq))
+    qsa.qsa_sparse_attn_backward(p, qq, t["k"], t["v"], idx, cnt, out, dout, dq, dk, dv, wsb,
+                                 q_pos0)
+    # a second call into fresh buffers reproduces the first bit for bit (the
+    # key side sums each key's rows in ascending row order)
+    dq2 = torch.empty_like(dq)
+    dk2, dv2 = torch.zeros_like(dk), torch.zeros_like(dv)
+    qsa.qsa_sparse_attn_backward(p, qq, t["k"], t["v"], idx, cnt, out, dout, dq2, dk2, dv2, wsb,
+                                 q_pos0)
     torch.cuda.synchronize()
     g_idx, g_cnt = to_host(idx), to_host(cnt)
     g_dq, g_dk, g_dv = dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
     pos = q_pos0 + np.arange(n_q)
     for b in range(B):
         dout_f = inputs.bf16_bits_to_f32(dout_h[b]).astype(np.float64)

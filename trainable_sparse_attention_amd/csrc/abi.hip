@@ -371,7 +371,8 @@ qsa_status qsa_sparse_attn_backward(const qsa_params* p, qsa_dtype dtype, const 
                                     const int32_t* idx, const int32_t* cnt, const void* out,
                                     const void* dout, int32_t B, int32_t n_q, int64_t q_pos0,
                                     int32_t hq, int32_t hkv, int32_t d, float scale, float* dq,
-                                    float* dk, float* dv, void* stream) {
+                                    float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
   qsa_status s = check_attn(p, dtype, q, k, v, idx, cnt, dq, B, n_q, hq, hkv, d, n_cap);
   if (s) return s;
   if (dtype != QSA_BF16) return fail(QSA_ERR_UNSUPPORTED, "the backward is built for bf16");
@@ -379,7 +380,13 @@ qsa_status qsa_sparse_attn_backward(const qsa_params* p, qsa_dtype dtype, const 
   if (q_pos0 < 0 || q_pos0 + n_q > n_cap)
     return fail(QSA_ERR_SHAPE, "positions [%lld, %lld) exceed n_cap=%lld", (long long)q_pos0,
                 (long long)(q_pos0 + n_q), (long long)n_cap);
+  // the transposed selection counts rows in 32-bit integers
+  if ((int64_t)n_q * qsa_k_blocks(p) > INT32_MAX)
+    return fail(QSA_ERR_UNSUPPORTED, "n_q * k_B beyond 2^31 entries per sequence");
   if (B == 0) return QSA_OK;
+  const size_t need = attn_backward_workspace(B, n_q, q_pos0, hq, p->r, qsa_k_blocks(p));
+  if (!workspace || workspace_bytes < need)
+    return fail(QSA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   AttnArgs a = {};
   a.q = q;
   a.k = k;
@@ -396,8 +403,14 @@ qsa_status qsa_sparse_attn_backward(const qsa_params* p, qsa_dtype dtype, const 
   a.kB = qsa_k_blocks(p);
   a.r = p->r;
   a.scale = scale > 0.f ? scale : 1.f / sqrtf((float)d);
-  return launched(launch_attn_backward(a, dout, dq, dk, dv, (hipStream_t)stream),
+  return launched(launch_attn_backward(a, dout, dq, dk, dv, workspace, (hipStream_t)stream),
                   "sparse_attn_backward");
+}
+
+size_t qsa_sparse_attn_backward_workspace(const qsa_params* p, int32_t B, int32_t n_q,
+                                          int64_t q_pos0, int32_t hq) {
+  if (!p || check_params(p) || B < 0 || n_q < 1 || hq < 1 || q_pos0 < 0) return 0;
+  return attn_backward_workspace(B, n_q, q_pos0, hq, p->r, qsa_k_blocks(p));
 }
 
 qsa_status qsa_index_distill(const qsa_params* p, qsa_dtype dtype, const void* q, const void* k,

@@ -3,20 +3,27 @@
 // Sparse Attention", Figure 3 for the token sets).  The block selection is a
 // discrete choice and receives no gradient.
 //
-// One 64-lane wave per (sequence, query row, KV head), as in the forward: the
-// hq/hkv query heads of the KV head are the 16 columns of the MFMA tiles.
-// The row's token set is walked twice in chunks of 32 keys, each chunk's K
-// and V copied into LDS (1 KB per global->LDS instruction):
-//   pass 1: S^T = K Q^T (v_mfma_f32_16x16x32_bf16), per-column log-sum-exp;
-//   pass 2: S^T again, P^T = 2^(S^T log2(e) scale - lse), dP^T = V dO^T,
-//           dS^T = P^T (dP^T - Dsum) with Dsum = <dO, O> per head,
-//           dQ^T += K^T dS^T (K^T read transposed from LDS, dS^T as the B
-//           operand under the same key permutation as P in the forward),
-//           dV^T = dO^T P and dK^T = Q^T dS (v_mfma_f32_16x16x16_bf16, P and
-//           dS transposed through a small LDS tile), added to dv / dk with
-//           float atomics (a key row is shared by every query that selected
-//           its block).
-// Inputs bf16; dq written, dk and dv accumulated, all float32.
+// The gradient of a key row gathers over every query that attended it, so
+// the work is split by who owns the output:
+//   query side, one 64-lane wave per (sequence, query row, KV head), as in
+//   the forward (the hq/hkv query heads of the KV head are the 16 columns
+//   of the MFMA tiles); the row's token set is walked twice in chunks of 32
+//   keys, each chunk's K and V copied into LDS:
+//     pass 1: S^T = K Q^T (v_mfma_f32_16x16x32_bf16), per-head log-sum-exp;
+//     pass 2: S^T again, P^T = 2^(S^T log2(e) scale - lse), dP^T = V dO^T,
+//             dS^T = P^T (dP^T - Dsum) with Dsum = <dO, O> per head, and
+//             dQ^T += K^T dS^T (K^T read transposed from LDS);
+//     the row's lse and Dsum per head go to the workspace.
+//   the selection transposed: per sequence, the rows that selected each
+//   block, as lists in ascending row order (count, scan, scatter, sort);
+//   key side, one wave per (sequence, KV head, block): the block's r keys
+//   against its rows, 16 (row, head) pairs at a time staged in LDS:
+//     S = Q K^T and dP = dO V^T (16x16x32), P and dS from the staged lse and
+//     Dsum, then dK^T += Q^T dS and dV^T += dO^T P (v_mfma_f32_16x16x16_bf16,
+//     Q^T and dO^T read transposed from LDS); the rows whose incomplete block
+//     is this one add their tails (key position <= row position).  A key
+//     row is owned by one wave, so dK and dV take one plain add each.
+// Inputs bf16; dq written, dk and dv added to, all float32.
 #include <math.h>
 
 #include "qsa_internal.h"
@@ -32,6 +39,7 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBwdKeys = 32;  // keys per chunk
+constexpr int kSortCap = 16384;  // longest block row list sorted in LDS
 
 // chunk c of key row kk at c ^ 2(kk & 7) (rows read straight and transposed)
 __device__ __forceinline__ int bswz(int kk, int c) { return c ^ ((kk & 7) << 1); }
@@ -51,15 +59,24 @@ __device__ __forceinline__ float xsum(float x) {
 
 }  // namespace
 
-// RR: tokens per block (r); SPC = 32 / RR slots per chunk.
+struct BwdWs {
+  float* lse;      // [B][n_q][hq] base-2 log-sum-exp of the scaled logits
+  float* dsum;     // [B][n_q][hq] <dout, out>
+  int32_t* cnt;    // [B][nbk + 1] rows per block, then the scatter's cursors
+  int32_t* off;    // [B][nbk + 1] start of each block's row list
+  int32_t* rows;   // [B][ld] the row lists, block after block
+  int64_t nbk;     // blocks holding keys some row attends
+  int64_t ld;      // list entries per sequence (n_q * k_B)
+};
+
+// Query side.  RR: tokens per block (r); SPC = 32 / RR slots per chunk.
 template <int RR>
-__global__ __launch_bounds__(64) void attn_bwd_kernel(AttnArgs a, const unsigned short* dout,
-                                                      float* dq, float* dk, float* dv) {
+__global__ __launch_bounds__(64) void attn_bwd_q_kernel(AttnArgs a, const unsigned short* dout,
+                                                        float* dq, float* lse_out,
+                                                        float* dsum_out) {
   constexpr int SPC = kBwdKeys / RR;
   __shared__ __attribute__((aligned(16))) unsigned short kl[kBwdKeys * 128];
   __shared__ __attribute__((aligned(16))) unsigned short vl[kBwdKeys * 128];
-  __shared__ __attribute__((aligned(16))) unsigned short pl[kBwdKeys * 16];   // P[key][head]
-  __shared__ __attribute__((aligned(16))) unsigned short dsl[kBwdKeys * 16];  // dS[key][head]
   const int lane = threadIdx.x, hl = lane & 15, gq = lane >> 4;
   int64_t w = blockIdx.x;
   const int g = (int)(w % a.hkv);
@@ -77,15 +94,15 @@ __global__ __launch_bounds__(64) void attn_bwd_kernel(AttnArgs a, const unsigned
   const int32_t* ids = a.idx + ((int64_t)b * a.n_q + t) * a.kB;
   const char* kb = (const char*)a.k + ((int64_t)b * a.hkv + g) * a.n_cap * 256;
   const char* vb = (const char*)a.v + ((int64_t)b * a.hkv + g) * a.n_cap * 256;
-  const int64_t rowq = (((int64_t)b * a.n_q + t) * a.hq + head) * 128;
+  const int64_t rowh = ((int64_t)b * a.n_q + t) * a.hq + head;  // (row, head) index
+  const int64_t rowq = rowh * 128;
 
   auto slot_ntok = [&](int u) { return u < cnt ? RR : (u < nslots ? ntail : 0); };
   auto slot_blk = [&](int u) -> int64_t { return u < cnt ? (int64_t)ids[u] : nb; };
   // key kk of the chunk at slot s: in the set?
   auto key_ok = [&](int s, int kk) { return kk % RR < slot_ntok(s + kk / RR); };
 
-  // Q^T and dO^T as B operands (column hl = head, dims 32cc + 8gq) and as
-  // the A operands of the 16x16x16 products (dim row, heads 4gq .. + 3)
+  // Q^T and dO^T as B operands (column hl = head, dims 32cc + 8gq)
   bf16x8 qb[4], ob[4];
   float dsum = 0.f;
   {
@@ -107,22 +124,6 @@ __global__ __launch_bounds__(64) void attn_bwd_kernel(AttnArgs a, const unsigned
     }
   }
   dsum = xsum(dsum);  // <dO, O> of head hl
-  // (bf16 bit patterns: the 16x16x16 product takes 16-bit integer vectors)
-  s16x4 qa[8], oa[8];
-  {
-    const int h0 = g * G + 4 * gq;
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      const int dim = 16 * tt + hl;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool ok = 4 * gq + e < G;
-        const int64_t off = (((int64_t)b * a.n_q + t) * a.hq + (ok ? h0 + e : 0)) * 128 + dim;
-        qa[tt][e] = ok ? (short)((const unsigned short*)a.q)[off] : (short)0;
-        oa[tt][e] = ok ? (short)dout[off] : (short)0;
-      }
-    }
-  }
 
   // chunk at slot s: K and V into LDS (instruction i moves keys 4i .. 4i+3)
   auto load_chunk = [&](int s, bool with_v) {
@@ -183,28 +184,29 @@ __global__ __launch_bounds__(64) void attn_bwd_kernel(AttnArgs a, const unsigned
   }
   const float mm = xmax(m);
   const float lse = mm + log2f(xsum(m == -INFINITY ? 0.f : l * exp2f(m - mm)));
+  if (hv && gq == 0) {
+    lse_out[rowh] = lse;
+    dsum_out[rowh] = dsum;
+  }
 
-  // ---- pass 2: gradients -------------------------------------------------
+  // ---- pass 2: dq --------------------------------------------------------
   f32x4 dqa[8];
 #pragma unroll
   for (int tt = 0; tt < 8; ++tt) dqa[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float* dkb = dk + ((int64_t)b * a.hkv + g) * a.n_cap * 128;
-  float* dvb = dv + ((int64_t)b * a.hkv + g) * a.n_cap * 128;
   for (int c = 0; c < nch; ++c) {
     const int s = SPC * c;
     load_chunk(s, true);
     f32x4 sacc[2], dpacc[2];
     rows_times(kl, qb, sacc);
     rows_times(vl, ob, dpacc);
-    // P and dS for column hl, keys 16kt + 4gq + i
-    float p[8], ds[8];
+    // dS for column hl, keys 16kt + 4gq + i
+    float ds[8];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool ok = hv && key_ok(s, 16 * kt + 4 * gq + i);
         const float pv = ok ? exp2f(sacc[kt][i] * sl2 - lse) : 0.f;
-        p[4 * kt + i] = pv;
         ds[4 * kt + i] = pv * (dpacc[kt][i] - dsum);
       }
     // dQ^T += K^T dS^T: B = dS^T with k index 8gq + j <-> key
@@ -225,41 +227,6 @@ __global__ __launch_bounds__(64) void attn_bwd_kernel(AttnArgs a, const unsigned
                                                           dqa[tt], 0, 0, 0);
       }
     }
-    // P and dS transposed through LDS: [key][head]
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = 16 * kt + 4 * gq + i;
-        pl[key * 16 + hl] = __builtin_bit_cast(unsigned short, (__bf16)p[4 * kt + i]);
-        dsl[key * 16 + hl] = __builtin_bit_cast(unsigned short, (__bf16)ds[4 * kt + i]);
-      }
-    __syncthreads();
-    // dV^T = dO^T P, dK^T = scale Q^T dS: 16 dims x 16 keys per call, k =
-    // 16 heads; lane (key hl, dims 4gq + e)
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int key = 16 * kt + hl;
-      const s16x4 pb = *(const s16x4*)(pl + key * 16 + 4 * gq);
-      const s16x4 db = *(const s16x4*)(dsl + key * 16 + 4 * gq);
-      const int u = s + key / RR;
-      const bool ok = key_ok(s, key);
-      const int64_t row = ok ? slot_blk(u) * RR + key % RR : 0;
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 dva = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(oa[tt], pb, z, 0, 0, 0);
-        const f32x4 dka = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qa[tt], db, z, 0, 0, 0);
-        if (ok) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int dim = 16 * tt + 4 * gq + e;
-            unsafeAtomicAdd(dvb + row * 128 + dim, dva[e]);
-            unsafeAtomicAdd(dkb + row * 128 + dim, dka[e] * a.scale);
-          }
-        }
-      }
-    }
     __syncthreads();
   }
   // dQ^T tile tt: lane (head hl, dims 16tt + 4gq + e)
@@ -273,33 +240,311 @@ __global__ __launch_bounds__(64) void attn_bwd_kernel(AttnArgs a, const unsigned
   }
 }
 
-hipError_t launch_attn_backward(const AttnArgs& a, const void* dout, float* dq, float* dk,
-                                float* dv, hipStream_t st) {
+// ---- the selection transposed ----------------------------------------------
+// Per sequence: cnt[j] rows selected block j, off[j] the start of block j's
+// list in rows[] (off[nbk] = the sequence's total), rows[] the row indices.
+
+__global__ __launch_bounds__(256) void bwd_clear_kernel(int32_t* p, int64_t n) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256)
+    p[e] = 0;
+}
+
+// one wave per query row: count (or, with scatter, place) its selected blocks
+template <bool SCATTER>
+__global__ __launch_bounds__(256) void bwd_count_kernel(AttnArgs a, BwdWs w) {
+  const int lane = threadIdx.x & 63;
+  const int64_t rows = (int64_t)a.B * a.n_q;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows;
+       row += (int64_t)gridDim.x * 4) {
+    const int b = (int)(row / a.n_q), t = (int)(row % a.n_q);
+    const int c = a.cnt[row];
+    const int32_t* ids = a.idx + row * a.kB;
+    int32_t* cb = w.cnt + (int64_t)b * (w.nbk + 1);
+    for (int u = lane; u < c; u += 64) {
+      const int j = ids[u];
+      if (j < 0 || j >= w.nbk) continue;  // not a block of these rows (never from index_topk)
+      if (SCATTER) {
+        const int at = atomicAdd(&cb[j], 1);
+        w.rows[(int64_t)b * w.ld + at] = t;
+      } else {
+        atomicAdd(&cb[j], 1);
+      }
+    }
+  }
+}
+
+// one workgroup per sequence: off = exclusive scan of cnt; cnt = off (the
+// scatter's cursors)
+__global__ __launch_bounds__(1024) void bwd_scan_kernel(BwdWs w) {
+  __shared__ int32_t wsum[16];
+  __shared__ int32_t carry;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int32_t* cb = w.cnt + (int64_t)blockIdx.x * (w.nbk + 1);
+  int32_t* ob = w.off + (int64_t)blockIdx.x * (w.nbk + 1);
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int64_t j0 = 0; j0 <= w.nbk; j0 += 1024) {
+    const int64_t j = j0 + tid;
+    const int32_t v = j < w.nbk ? cb[j] : 0;
+    int32_t incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int32_t before = carry;
+    for (int x = 0; x < wv; ++x) before += wsum[x];
+    if (j <= w.nbk) {
+      ob[j] = before + incl - v;
+      cb[j] = before + incl - v;
+    }
+    __syncthreads();
+    if (tid == 1023) carry = before + incl;
+    __syncthreads();
+  }
+}
+
+// one workgroup per (sequence, block): the block's list in ascending row
+// order (a bitonic sort in LDS), so that the key side sums in a fixed order;
+// longer lists than kSortCap stay in the scatter's order
+__global__ __launch_bounds__(1024) void bwd_sort_kernel(BwdWs w) {
+  __shared__ int32_t v[kSortCap];
+  const int tid = threadIdx.x;
+  const int64_t b = blockIdx.x / w.nbk, j = blockIdx.x % w.nbk;
+  const int32_t* ob = w.off + b * (w.nbk + 1);
+  const int32_t o0 = ob[j], L = ob[j + 1] - o0;
+  if (L < 2 || L > kSortCap) return;
+  int n2 = 2;
+  while (n2 < L) n2 <<= 1;
+  int32_t* src = w.rows + b * w.ld + o0;
+  for (int e = tid; e < n2; e += 1024) v[e] = e < L ? src[e] : 0x7fffffff;
+  __syncthreads();
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int e = tid; e < n2; e += 1024) {
+        const int p = e ^ jj;
+        if (p > e) {
+          const bool up = (e & k) == 0;
+          const int32_t x = v[e], y = v[p];
+          if ((x > y) == up) {
+            v[e] = y;
+            v[p] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int e = tid; e < L; e += 1024) src[e] = v[e];
+}
+
+// Key side.  One wave per (sequence, KV head, block j).  16 (row, head) pairs
+// per step: RB = floor(16 / G) rows, pair i = (row i / G, head g G + i % G);
+// Q and dO rows staged in LDS [pair][128] under the bswz swizzle.
+template <int RR>
+__global__ __launch_bounds__(64) void attn_bwd_kv_kernel(AttnArgs a, const unsigned short* dout,
+                                                         BwdWs w, float* dk, float* dv) {
+  __shared__ __attribute__((aligned(16))) unsigned short ql[16 * 128];
+  __shared__ __attribute__((aligned(16))) unsigned short ol[16 * 128];
+  __shared__ float lsel[16], dsl[16];
+  __shared__ int32_t rowl[16];
+  const int lane = threadIdx.x, hl = lane & 15, gq = lane >> 4;
+  int64_t wi = blockIdx.x;
+  const int64_t j = wi % w.nbk;
+  wi /= w.nbk;
+  const int g = (int)(wi % a.hkv);
+  const int b = (int)(wi / a.hkv);
+  const int G = a.hq / a.hkv;
+  const int RB = 16 / G;
+  const int64_t key0 = j * RR;  // first key position of the block
+  // the block's rows: its list, then the rows whose incomplete block it is
+  // (positions key0 .. key0 + RR - 2 within the call's rows)
+  const int32_t* ob = w.off + (int64_t)b * (w.nbk + 1);
+  const int32_t L = ob[j + 1] - ob[j];
+  const int32_t* list = w.rows + (int64_t)b * w.ld + ob[j];
+  const int64_t tp0 = key0 > a.q_pos0 ? key0 : a.q_pos0;
+  int64_t tp1 = key0 + RR - 2;
+  if (tp1 > a.q_pos0 + a.n_q - 1) tp1 = a.q_pos0 + a.n_q - 1;
+  const int ntr = tp1 >= tp0 ? (int)(tp1 - tp0 + 1) : 0;
+  const int total = L + ntr;
+  if (total == 0) return;
+  const char* kb = (const char*)a.k + ((int64_t)b * a.hkv + g) * a.n_cap * 256;
+  const char* vb = (const char*)a.v + ((int64_t)b * a.hkv + g) * a.n_cap * 256;
+  // K and V of the block as B operands: column hl = key hl (zero past RR
+  // and past the cache's end), dims 32c + 8gq
+  const bool kin = hl < RR && key0 + hl < a.n_cap;
+  bf16x8 kf[4], vf[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0}, y = x;
+    if (kin) {
+      x = *(const u16x8*)(kb + (key0 + hl) * 256 + (32 * c + 8 * gq) * 2);
+      y = *(const u16x8*)(vb + (key0 + hl) * 256 + (32 * c + 8 * gq) * 2);
+    }
+    kf[c] = __builtin_bit_cast(bf16x8, x);
+    vf[c] = __builtin_bit_cast(bf16x8, y);
+  }
+  f32x4 dka[8], dva[8];
+#pragma unroll
+  for (int tt = 0; tt < 8; ++tt) dka[tt] = dva[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float sl2 = a.scale * 1.4426950408889634f;
+  const unsigned short* qg = (const unsigned short*)a.q;
+  for (int n0 = 0; n0 < total; n0 += RB) {
+    // the step's rows (-1: none)
+    if (lane < 16) {
+      int32_t t = -1;
+      if (lane < RB && n0 + lane < total)
+        t = n0 + lane < L ? list[n0 + lane] : (int32_t)(tp0 - a.q_pos0) + (n0 + lane - L);
+      rowl[lane] = t;
+    }
+    __syncthreads();
+    // pairs 4i + lane / 16 of instruction i: chunk lane & 15 of its Q and dO
+    // rows (zero rows are read from row 0 of the sequence and masked below)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pr = 4 * i + (lane >> 4);
+      const int rr = pr / G;
+      const int32_t t = rr < RB ? rowl[rr] : -1;
+      const int64_t rh = ((int64_t)b * a.n_q + (t >= 0 ? t : 0)) * a.hq + g * G + pr % G;
+      const uint64_t off = (uint64_t)rh * 256 + 16 * bswz(pr, lane & 15);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)((const char*)qg + off),
+                                       (lds_void_t*)(ql + i * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)((const char*)dout + off),
+                                       (lds_void_t*)(ol + i * 512), 16, 0, 0);
+    }
+    if (lane < 16) {
+      const int rr = lane / G;
+      const int32_t t = rr < RB ? rowl[rr] : -1;
+      float x = 0.f, y = 0.f;
+      if (t >= 0) {
+        const int64_t rh = ((int64_t)b * a.n_q + t) * a.hq + g * G + lane % G;
+        x = w.lse[rh];
+        y = w.dsum[rh];
+      }
+      lsel[lane] = x;
+      dsl[lane] = y;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    // S = Q K^T, dP = dO V^T: lane (key hl, pairs 4gq + e)
+    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, dpa = sa;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bf16x8 qa = *(const bf16x8*)(ql + hl * 128 + 8 * bswz(hl, 4 * c + gq));
+      const bf16x8 oa = *(const bf16x8*)(ol + hl * 128 + 8 * bswz(hl, 4 * c + gq));
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[c], sa, 0, 0, 0);
+      dpa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, vf[c], dpa, 0, 0, 0);
+    }
+    s16x4 pb, db;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int pr = 4 * gq + e, rr = pr / G;
+      const int32_t t = rr < RB ? rowl[rr] : -1;
+      // a listed row attends the whole block; a tail row the keys up to
+      // its own position
+      const bool ok = kin && t >= 0 && (n0 + rr < L || key0 + hl <= a.q_pos0 + t);
+      const float p = ok ? exp2f(sa[e] * sl2 - lsel[pr]) : 0.f;
+      const float d = p * (dpa[e] - dsl[pr]);
+      pb[e] = __builtin_bit_cast(short, (__bf16)p);
+      db[e] = __builtin_bit_cast(short, (__bf16)d);
+    }
+    // dK^T += Q^T dS, dV^T += dO^T P: A = Q^T / dO^T read transposed (dims
+    // 16tt + hl, pairs 4gq .. 4gq + 3), B = dS / P (pairs, key hl)
+    {
+      const int kk = 4 * gq + (hl >> 2);
+      const int e0 = 4 * (hl & 1);
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        const int ch = 2 * tt + ((hl & 3) >> 1);
+        const s16x4 qt = tr16(ql + kk * 128 + bswz(kk, ch) * 8 + e0);
+        const s16x4 ot = tr16(ol + kk * 128 + bswz(kk, ch) * 8 + e0);
+        dka[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qt, db, dka[tt], 0, 0, 0);
+        dva[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ot, pb, dva[tt], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  // dK^T tile tt: lane (key hl, dims 16tt + 4gq + e); one owner per key row
+  if (kin) {
+    const int64_t row = ((int64_t)b * a.hkv + g) * a.n_cap + key0 + hl;
+    float* dkr = dk + row * 128;
+    float* dvr = dv + row * 128;
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      const int d0 = 16 * tt + 4 * gq;
+      f32x4 x = *(f32x4*)(dkr + d0), y = *(f32x4*)(dvr + d0);
+      x += dka[tt] * a.scale;
+      y += dva[tt];
+      *(f32x4*)(dkr + d0) = x;
+      *(f32x4*)(dvr + d0) = y;
+    }
+  }
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static BwdWs carve_bwd(void* ws, int B, int n_q, int64_t q_pos0, int hq, int r, int kB,
+                       size_t* total) {
+  BwdWs w;
+  w.nbk = (q_pos0 + n_q) / r + 1;
+  w.ld = (int64_t)n_q * kB;
+  char* p = (char*)ws;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* q = p ? p + off : nullptr;
+    off += align256(bytes);
+    return q;
+  };
+  w.lse = (float*)take((size_t)B * n_q * hq * sizeof(float));
+  w.dsum = (float*)take((size_t)B * n_q * hq * sizeof(float));
+  w.cnt = (int32_t*)take((size_t)B * (w.nbk + 1) * sizeof(int32_t));
+  w.off = (int32_t*)take((size_t)B * (w.nbk + 1) * sizeof(int32_t));
+  w.rows = (int32_t*)take((size_t)B * w.ld * sizeof(int32_t));
+  if (total) *total = off;
+  return w;
+}
+
+size_t attn_backward_workspace(int B, int n_q, int64_t q_pos0, int hq, int r, int kB) {
+  size_t total = 0;
+  carve_bwd(nullptr, B, n_q, q_pos0, hq, r, kB, &total);
+  return total;
+}
+
+template <int RR>
+static hipError_t launch_bwd_r(const AttnArgs& a, const unsigned short* d, float* dq, float* dk,
+                               float* dv, const BwdWs& w, hipStream_t st) {
   const int64_t waves = (int64_t)a.B * a.n_q * a.hkv;
-  if (waves == 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_bwd_q_kernel<RR>, dim3((unsigned)waves), dim3(64), 0, st, a, d, dq,
+                     w.lse, w.dsum);
+  const int64_t rows = (int64_t)a.B * a.n_q;
+  const unsigned cg = (unsigned)((rows + 3) / 4 < 65536 ? (rows + 3) / 4 : 65536);
+  const int64_t ncnt = (int64_t)a.B * (w.nbk + 1);
+  hipLaunchKernelGGL(bwd_clear_kernel, dim3((unsigned)((ncnt + 255) / 256 < 4096
+                                                           ? (ncnt + 255) / 256 : 4096)),
+                     dim3(256), 0, st, w.cnt, ncnt);
+  hipLaunchKernelGGL(bwd_count_kernel<false>, dim3(cg), dim3(256), 0, st, a, w);
+  hipLaunchKernelGGL(bwd_scan_kernel, dim3((unsigned)a.B), dim3(1024), 0, st, w);
+  hipLaunchKernelGGL(bwd_count_kernel<true>, dim3(cg), dim3(256), 0, st, a, w);
+  hipLaunchKernelGGL(bwd_sort_kernel, dim3((unsigned)(a.B * w.nbk)), dim3(1024), 0, st, w);
+  hipLaunchKernelGGL(attn_bwd_kv_kernel<RR>, dim3((unsigned)(a.B * a.hkv * w.nbk)), dim3(64), 0,
+                     st, a, d, w, dk, dv);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_backward(const AttnArgs& a, const void* dout, float* dq, float* dk,
+                                float* dv, void* ws, hipStream_t st) {
+  if ((int64_t)a.B * a.n_q * a.hkv == 0) return hipSuccess;
+  const BwdWs w = carve_bwd(ws, a.B, a.n_q, a.q_pos0, a.hq, a.r, a.kB, nullptr);
   const unsigned short* d = (const unsigned short*)dout;
   switch (a.r) {
-    case 1:
-      hipLaunchKernelGGL(attn_bwd_kernel<1>, dim3((unsigned)waves), dim3(64), 0, st, a, d, dq, dk,
-                         dv);
-      break;
-    case 2:
-      hipLaunchKernelGGL(attn_bwd_kernel<2>, dim3((unsigned)waves), dim3(64), 0, st, a, d, dq, dk,
-                         dv);
-      break;
-    case 8:
-      hipLaunchKernelGGL(attn_bwd_kernel<8>, dim3((unsigned)waves), dim3(64), 0, st, a, d, dq, dk,
-                         dv);
-      break;
-    case 16:
-      hipLaunchKernelGGL(attn_bwd_kernel<16>, dim3((unsigned)waves), dim3(64), 0, st, a, d, dq,
-                         dk, dv);
-      break;
-    default:
-      hipLaunchKernelGGL(attn_bwd_kernel<4>, dim3((unsigned)waves), dim3(64), 0, st, a, d, dq, dk,
-                         dv);
+    case 1: return launch_bwd_r<1>(a, d, dq, dk, dv, w, st);
+    case 2: return launch_bwd_r<2>(a, d, dq, dk, dv, w, st);
+    case 8: return launch_bwd_r<8>(a, d, dq, dk, dv, w, st);
+    case 16: return launch_bwd_r<16>(a, d, dq, dk, dv, w, st);
+    default: return launch_bwd_r<4>(a, d, dq, dk, dv, w, st);
   }
-  return hipGetLastError();
 }
 
 }  // namespace qsa

@@ -127,9 +127,12 @@ hipError_t launch_attn_prefill(qsa_dtype dt, const AttnArgs& a, hipStream_t st);
 // merge nsplit partials per (sequence, token, KV head) into a.out
 hipError_t launch_attn_combine(qsa_dtype dt, const AttnArgs& a, int nsplit, const float* part,
                                hipStream_t st);
-// sparse attention backward (bf16 inputs): dq written, dk / dv accumulated
+// sparse attention backward (bf16 inputs): dq written, dk / dv added to;
+// the workspace holds per-(row, head) lse and <dout, out> and the selection
+// transposed to per-block row lists
+size_t attn_backward_workspace(int B, int n_q, int64_t q_pos0, int hq, int r, int kB);
 hipError_t launch_attn_backward(const AttnArgs& a, const void* dout, float* dq, float* dk,
-                                float* dv, hipStream_t st);
+                                float* dv, void* ws, hipStream_t st);
 // indexer distillation (r = 4, bf16): loss and dq_idx written, dkbar added to
 struct DistillArgs {
   const unsigned short* q;      // [B][n_q][hq][128]

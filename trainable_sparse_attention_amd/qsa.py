@@ -22,7 +22,8 @@ EXPORTS = ["qsa_default_params", "qsa_k_blocks", "qsa_status_str", "qsa_last_err
            "qsa_index_topk_workspace",
            "qsa_sparse_attn_prefill", "qsa_sparse_attn_decode",
            "qsa_sparse_attn_decode_workspace", "qsa_sparse_attn_decode_shared",
-           "qsa_sparse_attn_decode_noalloc", "qsa_sparse_attn_backward", "qsa_index_distill",
+           "qsa_sparse_attn_decode_noalloc", "qsa_sparse_attn_backward",
+           "qsa_sparse_attn_backward_workspace", "qsa_index_distill",
            "qsa_pool_keys_backward",
            "qsa_dense_attn_prefill",
            "qsa_dense_attn_decode", "qsa_dense_attn_decode_workspace",
@@ -88,8 +89,10 @@ def lib():
                                                      I32, I32, I32, I32, I32, F, P, P]
         L.qsa_sparse_attn_decode_noalloc.restype = ctypes.c_int
         L.qsa_sparse_attn_backward.argtypes = [PP, ctypes.c_int, P, P, P, I64, P, P, P, P, I32,
-                                               I32, I64, I32, I32, I32, F, P, P, P, P]
+                                               I32, I64, I32, I32, I32, F, P, P, P, P, SZ, P]
         L.qsa_sparse_attn_backward.restype = ctypes.c_int
+        L.qsa_sparse_attn_backward_workspace.argtypes = [PP, I32, I32, I64, I32]
+        L.qsa_sparse_attn_backward_workspace.restype = SZ
         L.qsa_index_distill.argtypes = [PP, ctypes.c_int, P, P, I64, P, P, I64, I32, I32, I64, I32,
                                         I32, I32, F, P, P, P, P]
         L.qsa_index_distill.restype = ctypes.c_int
@@ -228,8 +231,12 @@ def qsa_sparse_attn_decode_noalloc(p, q, k_cache, v_cache, seq_len, idx, cnt, ou
                                                 hkv, d, scale, _ptr(out), _stream(stream)))
 
 
-def qsa_sparse_attn_backward(p, q, k, v, idx, cnt, out, dout, dq, dk, dv, q_pos0=0, scale=0.0,
-                             stream=None):
+def qsa_sparse_attn_backward_workspace(p, B, n_q, q_pos0, hq):
+    return lib().qsa_sparse_attn_backward_workspace(ctypes.byref(p), B, n_q, q_pos0, hq)
+
+
+def qsa_sparse_attn_backward(p, q, k, v, idx, cnt, out, dout, dq, dk, dv, workspace, q_pos0=0,
+                             scale=0.0, stream=None):
     """Gradients of the sparse attention (bf16 inputs): dq [B][n_q][hq][d]
     float32 written; dk, dv [B][hkv][n_cap][d] float32 added to."""
     B, n_q, hq, d = q.shape
@@ -237,7 +244,9 @@ def qsa_sparse_attn_backward(p, q, k, v, idx, cnt, out, dout, dq, dk, dv, q_pos0
     _check(lib().qsa_sparse_attn_backward(ctypes.byref(p), dtype_code(q), _ptr(q), _ptr(k),
                                           _ptr(v), n_cap, _ptr(idx), _ptr(cnt), _ptr(out),
                                           _ptr(dout), B, n_q, q_pos0, hq, hkv, d, scale, _ptr(dq),
-                                          _ptr(dk), _ptr(dv), _stream(stream)))
+                                          _ptr(dk), _ptr(dv), _ptr(workspace),
+                                          0 if workspace is None else workspace.numel(),
+                                          _stream(stream)))
 
 
 def qsa_index_distill(p, q, k, q_idx, kbar, loss, dq_idx, dkbar, q_pos0=0, scale=0.0,
