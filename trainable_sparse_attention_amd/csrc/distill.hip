@@ -20,8 +20,9 @@
 // queries carried as bf16 hi + lo (float-level accuracy), head sums and the
 // block maximum by lane shuffles.  Three passes over the history: the
 // teacher's log-sum-exp per head; the normalisers (sum of a_b, the
-// student's log-sum-exp) and the loss; the gradients.  dkbar is summed over
-// the workgroup's rows in LDS and added to global memory with float atomics.
+// student's log-sum-exp) and the loss; the gradients.  dkbar of a step's
+// blocks is one matrix product over the workgroup's (row, head) pairs (the
+// rotated queries stay in LDS), added to global memory with float atomics.
 //
 // Built for r = 4, bfloat16 inputs, hq <= 16, 4 indexer heads of 128 dims,
 // rope_dims <= 64.
@@ -40,6 +41,7 @@ constexpr int kDW = 8;         // waves (rows) per workgroup
 constexpr int kStepKeys = 64;  // keys per step
 constexpr int kStepBlk = 16;   // blocks per step (r = 4)
 constexpr int kMaxKv = 16;
+static_assert(kDW * 16 == 128, "one 16-dim slice of dkbar per wave");
 
 __device__ __forceinline__ int dswz(int kk, int c) { return c ^ (kk & 15); }
 
@@ -70,8 +72,9 @@ __global__ __launch_bounds__(64 * kDW) void distill_kernel(DistillArgs a) {
   // keys [16][128] bf16, then per-wave scratch, then the dkbar sums
   unsigned short* kls = (unsigned short*)smem_dist;
   unsigned short* kbs = kls + (size_t)a.hkv * kStepKeys * 128;
-  float* scr = (float*)(kbs + kStepBlk * 128);  // [kDW][4 * 128] rotated queries / [kDW][32]
-  float* dks = scr + kDW * 4 * 128;            // [16][128] dkbar partial sums
+  float* scr = (float*)(kbs + kStepBlk * 128);  // [kDW][4][128] rotated queries (kept)
+  float* wscr = scr + kDW * 4 * 128;           // [kDW][32] per-wave a and g values
+  float* gmat = wscr + kDW * 32;               // [16 blocks][kDW * 4]: g where the head's score > 0
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int hl = lane & 15, gq = lane >> 4;
@@ -142,14 +145,7 @@ __global__ __launch_bounds__(64 * kDW) void distill_kernel(DistillArgs a) {
     ib[cc] = __builtin_bit_cast(bf16x8, h);
     if (cc < 2) ibl[cc] = __builtin_bit_cast(bf16x8, lo);
   }
-  // the rotated query at this lane's dims (lane, lane + 64), all 4 heads
-  float qd[4][2];
-#pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    qd[h][0] = qs[h * 128 + lane];
-    qd[h][1] = qs[h * 128 + 64 + lane];
-  }
-  __syncthreads();  // scratch is reused below
+  __syncthreads();
 
   // ---- a step's K rows (every KV head) and pooled keys into LDS ---------
   const int nkv_ins = hkv * kStepKeys / 4;  // 1 KB instructions for K
@@ -231,7 +227,7 @@ __global__ __launch_bounds__(64 * kDW) void distill_kernel(DistillArgs a) {
 
   // per step: a_b and I_b of the step's 16 blocks; lane (hl, gq) ends with
   // a and I of blocks 4gq + i (i < 4) and the sign bits of the 4 heads
-  float* wsc = scr + wv * 32;  // this wave's [16] a values, then [16] g values
+  float* wsc = wscr + wv * 32;  // this wave's [16] a values, then [16] g values
   auto block_terms = [&](int64_t k0, float* av, float* iv, uint64_t* sgn) {
     // teacher: head-summed probabilities, maximum over the block's 4 keys
 #pragma unroll
@@ -312,11 +308,16 @@ __global__ __launch_bounds__(64 * kDW) void distill_kernel(DistillArgs a) {
         has ? alog / asum - logf(asum) - aI / asum + lnz : 0.f;
 
   // ---- pass 3: gradients -------------------------------------------------
+  // dq~ of each row stays in its wave's registers.  dkbar of the step's 16
+  // blocks is one small product over the workgroup's (row, head) pairs,
+  // C[b][d] = sum_(row, h) G[b][(row, h)] q~[(row, h)][d] with G = g_b where
+  // head h's score of block b is positive (else 0): every wave writes its
+  // row's 16 x 4 column of G to LDS, then wave wv forms dims 16 wv .. 16 wv
+  // + 15 of C on v_mfma_f32_16x16x4f32 (float operands, k = (row, head)).
   float dq[4][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
   const float inv_a = has ? 1.f / asum : 0.f;
   for (int st = 0; st < nstep2; ++st) {
     const int64_t k0 = (int64_t)st * kStepKeys;
-    for (int e = tid; e < kStepBlk * 128; e += 64 * kDW) dks[e] = 0.f;
     stage(k0, pos_last + 1, true);
     float av[4], iv[4];
     uint64_t sgn[4];
@@ -336,25 +337,35 @@ __global__ __launch_bounds__(64 * kDW) void distill_kernel(DistillArgs a) {
       const int i = bb & 3, grp = bb >> 2;
       const float k_lo = bf16_to_f32(kbs[bb * 128 + 8 * dswz(bb, lane >> 3) + (lane & 7)]);
       const float k_hi = bf16_to_f32(kbs[bb * 128 + 8 * dswz(bb, 8 + (lane >> 3)) + (lane & 7)]);
-      float c0 = 0.f, c1 = 0.f;
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         const bool on = (sgn[i] >> (16 * grp + h)) & 1ull;
         const float gh = on ? gb : 0.f;
         dq[h][0] += gh * k_lo;
         dq[h][1] += gh * k_hi;
-        c0 += gh * qd[h][0];
-        c1 += gh * qd[h][1];
       }
-      atomicAdd(&dks[bb * 128 + lane], c0);
-      atomicAdd(&dks[bb * 128 + 64 + lane], c1);
+    }
+    {
+      // this row's column of G: lane (block lane / 4, head lane % 4)
+      const int bb = lane >> 2, h = lane & 3, i = bb & 3, grp = bb >> 2;
+      const uint64_t sg = i == 0 ? sgn[0] : (i == 1 ? sgn[1] : (i == 2 ? sgn[2] : sgn[3]));
+      const bool on = (sg >> (16 * grp + h)) & 1ull;
+      gmat[bb * (kDW * 4) + wv * 4 + h] = on ? wsc[16 + bb] : 0.f;
     }
     __syncthreads();
-    // the workgroup's sums of this step's pooled-key gradients
-    for (int e = tid; e < kStepBlk * 128; e += 64 * kDW) {
-      const int64_t blk = (int64_t)st * kStepBlk + e / 128;
-      if (blk < nb_last && dks[e] != 0.f)
-        unsafeAtomicAdd(a.dkbar + ((int64_t)b * a.nb_cap + blk) * 128 + (e & 127), dks[e]);
+    f32x4 cacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kDW; ++c) {
+      const float ga = gmat[hl * (kDW * 4) + 4 * c + gq];
+      const float qv = scr[(4 * c + gq) * 128 + 16 * wv + hl];
+      cacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ga, qv, cacc, 0, 0, 0);
+    }
+    // lane holds blocks 4gq + e of the step at dim 16 wv + hl
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t blk = (int64_t)st * kStepBlk + 4 * gq + e;
+      if (blk < nb_last && cacc[e] != 0.f)
+        unsafeAtomicAdd(a.dkbar + ((int64_t)b * a.nb_cap + blk) * 128 + 16 * wv + hl, cacc[e]);
     }
     __syncthreads();
   }
@@ -382,7 +393,7 @@ __global__ __launch_bounds__(64 * kDW) void distill_kernel(DistillArgs a) {
 
 size_t distill_lds(int hkv) {
   return (size_t)hkv * kStepKeys * 128 * 2 + kStepBlk * 128 * 2 + kDW * 4 * 128 * 4 +
-         kStepBlk * 128 * 4;
+         kDW * 32 * 4 + kStepBlk * kDW * 4 * 4;
 }
 
 hipError_t launch_distill(const DistillArgs& a, hipStream_t st) {
