@@ -32,11 +32,16 @@ def _bf16(x):
     return inputs.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
 
 
-@pytest.mark.parametrize("r,n,K,q_pos0", [(4, 1200, 256, 0), (8, 1500, 512, 0),
-                                          (4, 2000, 512, 1300)])
-def test_sparse_attn_backward(r, n, K, q_pos0):
-    say("sparse attention backward r=%d n=%d K=%d q_pos0=%d" % (r, n, K, q_pos0))
-    B, hq, hkv = 2, 16, 2
+@pytest.mark.parametrize("r,n,K,q_pos0,hq,hkv", [(4, 1200, 256, 0, 16, 2), (8, 1500, 512, 0, 16, 2),
+                                                  (4, 2000, 512, 1300, 16, 2),
+                                                  (1, 700, 256, 0, 8, 2), (16, 3001, 512, 0, 16, 1),
+                                                  (2, 1003, 128, 500, 6, 2), (4, 777, 64, 0, 2, 2)])
+def test_sparse_attn_backward(r, n, K, q_pos0, hq, hkv):
+    """Query-side dq and key-side dk, dv (16 / G rows per key-side step:
+    G = hq / hkv of 8, 4, 16, 3 (not a divisor of 16) and 1)."""
+    say("sparse attention backward r=%d n=%d K=%d q_pos0=%d hq=%d hkv=%d" % (r, n, K, q_pos0, hq,
+                                                                          hkv))
+    B = 2
     d = inputs.small(B=B, n=n, hq=hq, hkv=hkv, dtype="bf16", r=r, K=K, seed=600 + r)
     p = qsa.params(r=r, K=K)
     kB = qsa.k_blocks(p)
