@@ -91,7 +91,7 @@ def test_sparse_attn_backward(r, n, K, q_pos0, hq, hkv):
 
 
 @pytest.mark.parametrize("n,q_pos0,hq,hkv", [(1000, 0, 16, 2), (1500, 900, 16, 2),
-                                             (777, 0, 8, 1)])
+                                             (777, 0, 8, 1), (900, 100, 16, 8)])
 def test_index_distill(n, q_pos0, hq, hkv):
     say("distillation n=%d q_pos0=%d hq=%d hkv=%d" % (n, q_pos0, hq, hkv))
     B = 2
