@@ -138,10 +138,11 @@ qsa_status qsa_pool_keys_rmsnorm(const qsa_params* p, qsa_dtype dtype, const voi
  * For each query row: the min(k_B, visible) blocks with the largest score
  * under the total order (score descending, block id ascending), written as
  * ascending block ids, padded with -1.  The score matrix is never stored.
- * Precision: with bfloat16 the score is a bf16 x bf16 contraction (the
- * rotated query rounded to bfloat16, round-to-nearest-even) accumulated in
- * float32; with float32 both operands stay float32.  Blocks whose scores
- * differ by less than the accumulation's rounding may be ordered either way.
+ * Precision: with bfloat16 the rotated query keeps float accuracy (each
+ * element carried as a bf16 high part plus a bf16 low part on the rotated
+ * dims) against the bf16 pooled keys, accumulated in float32; with float32
+ * both operands stay float32.  Blocks whose scores differ by less than the
+ * accumulation's rounding may be ordered either way.
  *
  *   q_idx : [B][n_q][h_idx][d_idx]  indexer queries, NOT rotated (h_idx
  *                                   is 1, 2 or 4)

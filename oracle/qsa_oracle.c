@@ -35,12 +35,7 @@
  *
  * Arithmetic: every input element is read as its exact stored value and all
  * arithmetic is in double.  Pooled keys are rounded once, round-to-nearest-
- * even, to the storage type.  Indexer queries are rotated in double; for
- * bfloat16 inputs the rotated query is then rounded to bfloat16 (round-to-
- * nearest-even), because the block score is a bf16 x bf16 contraction with a
- * float32 accumulator and the top-k decision is taken at that operand
- * precision (the accumulation stays exact here); float32 inputs keep the
- * unrounded rotated query.  Attention queries are never rounded.
+ * even, to the storage type.  Queries are rotated in double and NOT rounded.
  * No blocking, fusion or reordering beyond the definitions.
  */
 #include <math.h>
@@ -167,9 +162,6 @@ int64_t orc_scores(const void* q_row, const void* kbar, int dt, int h, int d, in
   double* q = (double*)malloc(sizeof(double) * (size_t)(h * d));
   for (int t = 0; t < h * d; ++t) q[t] = orc_ld(q_row, dt, t);
   for (int hh = 0; hh < h; ++hh) orc_rope(q + hh * d, R, theta, (double)pos);
-  /* bf16 contraction: the rotated query enters as a bf16 operand */
-  if (dt == ORC_BF16)
-    for (int t = 0; t < h * d; ++t) q[t] = orc_round(q[t], 8, -126, 3.3895313892515355e38);
   int64_t nb = orc_nvis(pos, r);
   for (int64_t b = 0; b < nb; ++b) {
     double s = 0.0;

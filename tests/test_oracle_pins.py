@@ -185,34 +185,6 @@ def test_scores_brute_force(r):
         np.testing.assert_allclose(s, _brute_scores(q[pos], kbar, pos, r), rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("r", [1, 4])
-def test_scores_bf16_round_the_rotated_query(r):
-    """bf16 inputs are scored as a bf16 x bf16 contraction: the rotated query
-    is rounded to bf16 before the product.  Checked against a matrix-product
-    route that rounds the rotated query through float32 by the bit rule of
-    the input generator; the unrounded route differs once the rotation is
-    not the identity, and agrees at position 0 where it is."""
-    rng = np.random.default_rng(40 + r)
-    n = 48
-    k = _bf16(rng.standard_normal((n, 128)))
-    kbar = oracle.pool(k, r=r)
-    q = _bf16(rng.standard_normal((n, 4, 128)))
-    ends = (np.arange(kbar.shape[0]) + 1) * r - 1
-    kb = _f(kbar).astype(np.float64)
-    for pos in range(n):
-        s = oracle.scores(q[pos], kbar, pos, r=r)
-        qr = oracle.rope_rows(_f(q[pos]).astype(np.float64), [pos] * 4, 64, 10000.0)
-        qr_b = _f(_bf16(qr.astype(np.float32))).astype(np.float64)
-        vis = kb[ends <= pos]
-        ref = np.maximum(qr_b @ vis.T, 0.0).sum(axis=0)
-        np.testing.assert_allclose(s, ref, rtol=1e-12, atol=1e-12)
-        unrounded = np.maximum(qr @ vis.T, 0.0).sum(axis=0)
-        if pos == 0:
-            np.testing.assert_allclose(s, unrounded, rtol=1e-12, atol=1e-12)
-        elif vis.shape[0]:
-            assert np.max(np.abs(s - unrounded)) > 1e-6 * np.max(np.abs(unrounded))
-
-
 def test_scores_relu_identity_heads_and_scaling():
     rng = np.random.default_rng(5)
     k = rng.standard_normal((256, 128)).astype(np.float32)

@@ -169,9 +169,8 @@ __global__ __launch_bounds__(kScanThreads) void index_decode_scan(IndexArgs a, D
   const int64_t hi = min(lo + (int64_t)w.chunk, nbmax);
   const T* kb = (const T*)a.kbar + (size_t)b * a.nb_cap * 128;
   if (lo >= hi) return;  // the whole workgroup: nothing to scan, nothing to count
-  // A operand rows 4t + h hold the rotated queries (zero for absent tokens),
-  // rounded to bf16; with NLO > 0 the rotated dims would also carry a bf16
-  // low part (split_bf16)
+  // A operand rows 4t + h hold the rotated queries (zero for absent tokens);
+  // bf16 keeps a low part for the rotated dims (see split_bf16)
   float vals[16 * 128 / kScanThreads];
 #pragma unroll
   for (int u = 0; u < 16 * 128 / kScanThreads; ++u) {
@@ -569,8 +568,14 @@ static hipError_t launch_scan_tpw(qsa_dtype dt, const IndexArgs& a, const Decode
                                   size_t lds, hipStream_t st) {
   if (dt != QSA_BF16)
     hipLaunchKernelGGL((index_decode_scan<float, 0, TPW>), g1, dim3(kScanThreads), lds, st, a, w);
-  else  // bf16 x bf16 contraction: rotated queries rounded to bf16 (NLO = 0)
+  else if (a.R == 0)
     hipLaunchKernelGGL((index_decode_scan<unsigned short, 0, TPW>), g1, dim3(kScanThreads), lds,
+                       st, a, w);
+  else if (a.R <= 64)
+    hipLaunchKernelGGL((index_decode_scan<unsigned short, 2, TPW>), g1, dim3(kScanThreads), lds,
+                       st, a, w);
+  else
+    hipLaunchKernelGGL((index_decode_scan<unsigned short, 4, TPW>), g1, dim3(kScanThreads), lds,
                        st, a, w);
   return hipGetLastError();
 }

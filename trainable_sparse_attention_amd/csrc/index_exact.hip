@@ -446,10 +446,12 @@ static hipError_t launch_t(const IndexArgs& a, void* ws, int num_cu, int g0, int
 hipError_t launch_index_exact(qsa_dtype dt, const IndexArgs& a, void* ws, int num_cu, int g0,
                               int count, const uint32_t* only, hipStream_t st) {
   if (a.n_q == 0 || a.B == 0 || count <= 0) return hipSuccess;
-  // bf16: a bf16 x bf16 contraction (the rotated queries rounded to bf16,
-  // no low parts: NLO = 0), the precision the selection is defined at
+  // NLO: 16-dim k-steps holding rotated dims, ceil(R / 16)
   if (dt != QSA_BF16) return launch_t<float, 0>(a, ws, num_cu, g0, count, only, st);
-  return launch_t<unsigned short, 0>(a, ws, num_cu, g0, count, only, st);
+  if (a.R == 0) return launch_t<unsigned short, 0>(a, ws, num_cu, g0, count, only, st);
+  if (a.R <= 32) return launch_t<unsigned short, 2>(a, ws, num_cu, g0, count, only, st);
+  if (a.R <= 64) return launch_t<unsigned short, 4>(a, ws, num_cu, g0, count, only, st);
+  return launch_t<unsigned short, 8>(a, ws, num_cu, g0, count, only, st);
 }
 
 }  // namespace qsa

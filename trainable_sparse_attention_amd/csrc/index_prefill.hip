@@ -4,9 +4,8 @@
 // "Qwen Sparse Attention": block-causal scores, top-K_B per query).
 //
 // Query rows go in tiles of 128: 16 waves of 8 rows, the rows of a wave being
-// one 32-row MFMA tile (8 queries x 4 heads) of rotated queries rounded to
-// bf16, held in registers (the template's NLO > 0 forms would add a bf16 low
-// part for the rotated dims).  Tiles run longest first, in groups whose candidate lists fit
+// one 32-row MFMA tile (8 queries x 4 heads) whose bf16 hi and lo parts stay
+// in registers.  Tiles run longest first, in groups whose candidate lists fit
 // the workspace.  Per group:
 //   1. scan (sample): tiles whose rows see more blocks than a list holds
 //      score a strided sample of m blocks, m = 16 visible / k_B (so that
@@ -111,7 +110,7 @@ __global__ __launch_bounds__(1024, 1) void index_scan_kernel(IndexArgs a, PipeWs
   // staged appends: (list entry, block id, score bits, unused)
   u32x4* bent = (u32x4*)(smem + 2 * kStageBytes) + wv * kBuf;
 
-  // ---- prologue: rotated queries -> the wave's A tile -------------------
+  // ---- prologue: rotated queries -> the wave's A tile (hi and lo) --------
   const int half = a.R / 2;
   {
     float2* table = (float2*)(smem + 2 * kStageBytes);  // [128][half]
@@ -438,7 +437,7 @@ static PipeWs carve(void* ws, int B, int n_q, int num_cu, size_t* total_bytes) {
   return w;
 }
 
-// bf16 with at most 64 rotated dims, and k_B small
+// bf16 with at most 64 rotated dims (lo parts in registers), and k_B small
 // enough that the lists hold a few times k_B
 static bool pipeline_covers(qsa_dtype dt, const IndexArgs& a) {
   return dt == QSA_BF16 && a.R <= 64 && a.kB <= kList / 3;
@@ -488,9 +487,10 @@ hipError_t launch_index_prefill(qsa_dtype dt, const IndexArgs& a, void* ws, int 
     return launch_index_exact(dt, a, ws, num_cu, 0, total, nullptr, st);
   }
   const PipeWs w = carve(ws, a.B, a.n_q, num_cu, nullptr);
-  // a bf16 x bf16 contraction: the rotated queries are rounded to bf16, with
-  // no low parts (NLO = 0), the precision the selection is defined at
-  return run_pipeline<0>(a, w, num_cu, st);
+  // NLO: 16-dim k-steps holding rotated dims, ceil(R / 16)
+  if (a.R == 0) return run_pipeline<0>(a, w, num_cu, st);
+  if (a.R <= 32) return run_pipeline<2>(a, w, num_cu, st);
+  return run_pipeline<4>(a, w, num_cu, st);
 }
 
 }  // namespace qsa
