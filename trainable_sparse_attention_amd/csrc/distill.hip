@@ -14,11 +14,13 @@
 // A workgroup of 8 waves takes 8 consecutive rows (one wave each) and walks
 // the history in lock step, 64 keys (16 blocks) a step; each step's K rows of
 // every KV head and the 16 pooled keys are copied once into LDS.  Per wave:
-// teacher logits S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (16 columns = the
-// query heads, one call per KV head, each column keeping its own head's
-// product), student scores on the same MFMA with the rotated indexer
-// queries carried as bf16 hi + lo (float-level accuracy), head sums and the
-// block maximum by lane shuffles.  Three passes over the history: the
+// teacher logits S = Q K^T on v_mfma_f32_16x16x32_bf16 (16 rows = the query
+// heads, one call per KV head, each row keeping its own head's product), so
+// that a lane holds one key against 4 heads: the head sum is 3 adds in the
+// lane and 2 shuffles across the lane groups, the block maximum 2 shuffles
+// within a lane quad.  Student scores on the same MFMA with the rotated
+// indexer queries carried as bf16 hi + lo (float-level accuracy).  Three
+// passes over the history: the
 // teacher's log-sum-exp per head; the normalisers (sum of a_b, the
 // student's log-sum-exp) and the loss; the gradients.  dkbar of a step's
 // blocks is one matrix product over the workgroup's (row, head) pairs (the
@@ -51,6 +53,12 @@ __device__ __forceinline__ float xsum16(float x) {  // over the 16 lanes of a gr
   x += __shfl_xor(x, 4);
   return x + __shfl_xor(x, 8);
 }
+__device__ __forceinline__ float xmax16(float x) {  // over the 16 lanes of a group
+  x = fmaxf(x, __shfl_xor(x, 1));
+  x = fmaxf(x, __shfl_xor(x, 2));
+  x = fmaxf(x, __shfl_xor(x, 4));
+  return fmaxf(x, __shfl_xor(x, 8));
+}
 __device__ __forceinline__ float xsum4(float x) {  // over lanes hl = 0..3 of a group
   x += __shfl_xor(x, 1);
   return x + __shfl_xor(x, 2);
@@ -66,7 +74,10 @@ __device__ __forceinline__ float xsumg(float x) {
 
 }  // namespace
 
-__global__ __launch_bounds__(64 * kDW) void distill_kernel(DistillArgs a) {
+// Two workgroups per CU (two waves per SIMD each) keep one workgroup's
+// compute running over the other's staging wait; that needs <= 128 VGPRs.
+__global__ __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(4))) void distill_kernel(
+    DistillArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_dist[];
   // K rows of the step: [hkv][64 keys][128] bf16, then the step's pooled
   // keys [16][128] bf16, then per-wave scratch, then the dkbar sums
@@ -174,55 +185,70 @@ __global__ __launch_bounds__(64 * kDW) void distill_kernel(DistillArgs a) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
-  // teacher logits (log2 units) of key tile kt (16 keys) of the step for
-  // column hl: lane (hl, gq) holds keys 16kt + 4gq + i
+  // teacher logits S = Q K^T of key tile kt (16 keys) of the step, scaled to
+  // log2 units: lane (hl, gq) holds key 16 kt + hl against heads 4 gq + i.
+  // One product per KV head; each of the lane's heads keeps its own KV
+  // head's value (heads >= hq keep 0 and are masked by the callers).
   auto teacher = [&](int kt, f32x4& out) {
-    const int gsel = hl < hq ? hl / G : 0;
     out = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int kk = 16 * kt + hl;
     for (int gg = 0; gg < hkv; ++gg) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const int kk = 16 * kt + hl;
       const unsigned short* rowp = kls + ((size_t)gg * kStepKeys + kk) * 128;
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
-        const bf16x8 av = *(const bf16x8*)(rowp + 8 * dswz(kk, 4 * cc + gq));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[cc], acc, 0, 0, 0);
+        const bf16x8 kv = *(const bf16x8*)(rowp + 8 * dswz(kk, 4 * cc + gq));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb[cc], kv, acc, 0, 0, 0);
       }
-      if (gg == gsel) out = acc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if ((4 * gq + i) / G == gg) out[i] = acc[i];
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) out[i] *= sl2;
   };
 
   // ---- pass 1: teacher log-sum-exp per head (base 2), keys 0 .. p -------
-  float lm = -INFINITY, ll = 0.f;
+  // per lane: a running maximum and sum for each of its 4 heads over the
+  // keys of its column hl; the 16 columns are merged after the sweep
+  float lm[4], ll[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lm[i] = -INFINITY;
+    ll[i] = 0.f;
+  }
   const int nstep1 = (int)((pos_last + 1 + kStepKeys - 1) / kStepKeys);
   for (int st = 0; st < nstep1; ++st) {
     const int64_t k0 = (int64_t)st * kStepKeys;
     stage(k0, pos_last + 1, false);
+    float x[4][4];  // [key tile][head], future keys at -inf
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       f32x4 s;
       teacher(kt, s);
+      const bool ok = live && k0 + 16 * kt + hl <= pos;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t key = k0 + 16 * kt + 4 * gq + i;
-        if (!live || key > pos) continue;
-        const float x = s[i];
-        if (x > lm) {
-          ll = ll * exp2f(lm - x) + 1.f;
-          lm = x;
-        } else {
-          ll += exp2f(x - lm);
-        }
+      for (int i = 0; i < 4; ++i) x[kt][i] = ok ? s[i] : -INFINITY;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float mx = fmaxf(fmaxf(lm[i], fmaxf(x[0][i], x[1][i])), fmaxf(x[2][i], x[3][i]));
+      if (mx != -INFINITY) {
+        float acc = lm[i] == -INFINITY ? 0.f : ll[i] * exp2f(lm[i] - mx);
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) acc += exp2f(x[kt][i] - mx);
+        ll[i] = acc;
+        lm[i] = mx;
       }
     }
     __syncthreads();
   }
-  float lse;
-  {
-    const float mm = xmaxg(lm);
-    lse = mm + log2f(xsumg(lm == -INFINITY ? 0.f : ll * exp2f(lm - mm)));
+  float lse[4];  // of heads 4 gq + i (-inf for absent rows and heads)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float mm = xmax16(lm[i]);
+    const float l = xsum16(lm[i] == -INFINITY ? 0.f : ll[i] * exp2f(lm[i] - mm));
+    lse[i] = mm == -INFINITY ? -INFINITY : mm + log2f(l);
   }
 
   // per step: a_b and I_b of the step's 16 blocks; lane (hl, gq) ends with
@@ -234,14 +260,16 @@ __global__ __launch_bounds__(64 * kDW) void distill_kernel(DistillArgs a) {
     for (int kt = 0; kt < 4; ++kt) {
       f32x4 s;
       teacher(kt, s);
-      float mx = 0.f;
+      const bool ok = live && k0 + 16 * kt + hl <= pos;
+      float sum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t key = k0 + 16 * kt + 4 * gq + i;
-        const float pr = (live && hl < hq && key <= pos) ? exp2f(s[i] - lse) : 0.f;
-        mx = fmaxf(mx, xsum16(pr));
-      }
-      if (hl == 0) wsc[4 * kt + gq] = mx;  // block 4kt + gq
+      for (int i = 0; i < 4; ++i)
+        sum += (ok && 4 * gq + i < hq) ? exp2f(s[i] - lse[i]) : 0.f;
+      sum = xsumg(sum);  // all heads of key 16 kt + hl
+      // block 4 kt + hl / 4: its 4 keys sit in lanes hl & ~3 .. (hl & ~3) + 3
+      float mx = fmaxf(sum, __shfl_xor(sum, 1));
+      mx = fmaxf(mx, __shfl_xor(mx, 2));
+      if (lane < 16 && (hl & 3) == 0) wsc[4 * kt + (hl >> 2)] = mx;
     }
     wave_sync();
     // student: 16 blocks x 4 heads (columns hl < 4)
