@@ -20,11 +20,12 @@
 // lane and 2 shuffles across the lane groups, the block maximum 2 shuffles
 // within a lane quad.  Student scores on the same MFMA with the rotated
 // indexer queries carried as bf16 hi + lo (float-level accuracy).  Three
-// passes over the history: the
-// teacher's log-sum-exp per head; the normalisers (sum of a_b, the
-// student's log-sum-exp) and the loss; the gradients.  dkbar of a step's
-// blocks is one matrix product over the workgroup's (row, head) pairs (the
-// rotated queries stay in LDS), added to global memory with float atomics.
+// passes over the history: the teacher's log-sum-exp per head; the
+// normalisers (sum of a_b, the student's log-sum-exp) and the loss; the
+// gradients.  Both gradients of a step are small float matrix products with
+// the step's g values over the workgroup's (row, head) pairs: dkbar of the
+// step's blocks (the rotated queries stay in LDS), added to global memory
+// with float atomics, and dq~, kept in registers.
 //
 // Built for r = 4, bfloat16 inputs, hq <= 16, 4 indexer heads of 128 dims,
 // rope_dims <= 64.
@@ -62,6 +63,13 @@ __device__ __forceinline__ float xmax16(float x) {  // over the 16 lanes of a gr
 __device__ __forceinline__ float xsum4(float x) {  // over lanes hl = 0..3 of a group
   x += __shfl_xor(x, 1);
   return x + __shfl_xor(x, 2);
+}
+__device__ __forceinline__ float xmax4(float x) {  // over lanes hl = 0..3 of a group
+  x = fmaxf(x, __shfl_xor(x, 1));
+  return fmaxf(x, __shfl_xor(x, 2));
+}
+__device__ __forceinline__ float sel4(const float* v, int i) {  // v[i] without scratch
+  return i == 0 ? v[0] : (i == 1 ? v[1] : (i == 2 ? v[2] : v[3]));
 }
 __device__ __forceinline__ float xmaxg(float x) {  // over the 4 lane groups
   x = fmaxf(x, __shfl_xor(x, 16));
@@ -301,33 +309,33 @@ __global__ __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(4))) v
     float av[4], iv[4];
     uint64_t sgn[4];
     block_terms(k0, av, iv, sgn);
-    if (hl == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t blk = (int64_t)st * kStepBlk + 4 * gq + i;
-        if (blk >= nb) continue;
-        asum += av[i];
-        alog += av[i] > 0.f ? av[i] * logf(av[i]) : 0.f;
-        aI += av[i] * iv[i];
-        if (iv[i] > zm) {
-          zl = zl * expf(zm - iv[i]) + 1.f;
-          zm = iv[i];
+    // lane (hl < 4, gq) takes block 4 gq + hl of the step
+    if (hl < 4) {
+      const float ab = sel4(av, hl), ib_ = sel4(iv, hl);
+      const int64_t blk = (int64_t)st * kStepBlk + 4 * gq + hl;
+      if (blk < nb) {
+        asum += ab;
+        alog += ab > 0.f ? ab * logf(ab) : 0.f;
+        aI += ab * ib_;
+        if (ib_ > zm) {
+          zl = zl * expf(zm - ib_) + 1.f;
+          zm = ib_;
         } else {
-          zl += expf(iv[i] - zm);
+          zl += expf(ib_ - zm);
         }
       }
     }
     __syncthreads();
   }
-  // combine the 4 lane groups (lanes hl = 0 carry the sums, others 0)
-  asum = xsumg(hl == 0 ? asum : 0.f);
-  alog = xsumg(hl == 0 ? alog : 0.f);
-  aI = xsumg(hl == 0 ? aI : 0.f);
+  // combine the 16 lanes hl < 4 (the others carry 0)
+  asum = xsumg(xsum4(hl < 4 ? asum : 0.f));
+  alog = xsumg(xsum4(hl < 4 ? alog : 0.f));
+  aI = xsumg(xsum4(hl < 4 ? aI : 0.f));
   float lnz;
   {
-    const float zz = hl == 0 ? zm : -INFINITY;
-    const float mz = xmaxg(zz);
-    const float s = xsumg(hl == 0 && zm != -INFINITY ? zl * expf(zm - mz) : 0.f);
+    const float zz = hl < 4 ? zm : -INFINITY;
+    const float mz = xmaxg(xmax4(zz));
+    const float s = xsumg(xsum4(hl < 4 && zm != -INFINITY ? zl * expf(zm - mz) : 0.f));
     lnz = mz + logf(s);
   }
   const bool has = live && nb > 0;
@@ -336,13 +344,17 @@ __global__ __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(4))) v
         has ? alog / asum - logf(asum) - aI / asum + lnz : 0.f;
 
   // ---- pass 3: gradients -------------------------------------------------
-  // dq~ of each row stays in its wave's registers.  dkbar of the step's 16
-  // blocks is one small product over the workgroup's (row, head) pairs,
-  // C[b][d] = sum_(row, h) G[b][(row, h)] q~[(row, h)][d] with G = g_b where
-  // head h's score of block b is positive (else 0): every wave writes its
-  // row's 16 x 4 column of G to LDS, then wave wv forms dims 16 wv .. 16 wv
-  // + 15 of C on v_mfma_f32_16x16x4f32 (float operands, k = (row, head)).
-  float dq[4][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
+  // Both gradients are small products with the step's G[b][(row, h)] = g_b
+  // where head h's score of block b is positive (else 0), over the
+  // workgroup's 8 rows x 4 heads: every wave writes its row's 16 x 4 column
+  // of G to LDS, then wave wv forms dims 16 wv .. 16 wv + 15 of
+  //   dkbar[b][d]     = sum_(row, h) G[b][(row, h)] q~[(row, h)][d]  (k = (row, h))
+  //   dq~[(row, h)][d] += sum_b kbar[b][d] G[b][(row, h)]            (k = b)
+  // on v_mfma_f32_16x16x4f32 (float operands).  dq~ stays in registers
+  // across the steps (dims of every row of the workgroup) and is regrouped
+  // by row through LDS at the end.
+  static_assert(kDW * 4 == 32, "two 16-column tiles of (row, head) pairs");
+  f32x4 dacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   const float inv_a = has ? 1.f / asum : 0.f;
   for (int st = 0; st < nstep2; ++st) {
     const int64_t k0 = (int64_t)st * kStepKeys;
@@ -350,29 +362,13 @@ __global__ __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(4))) v
     float av[4], iv[4];
     uint64_t sgn[4];
     block_terms(k0, av, iv, sgn);
-    // g of blocks 4gq + i, shared through the wave's scratch
-    if (hl == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t blk = (int64_t)st * kStepBlk + 4 * gq + i;
-        wsc[16 + 4 * gq + i] = (has && blk < nb) ? expf(iv[i] - lnz) - av[i] * inv_a : 0.f;
-      }
+    // g of block 4 gq + hl (lanes hl < 4), shared through the wave's scratch
+    if (hl < 4) {
+      const int64_t blk = (int64_t)st * kStepBlk + 4 * gq + hl;
+      wsc[16 + 4 * gq + hl] =
+          (has && blk < nb) ? expf(sel4(iv, hl) - lnz) - sel4(av, hl) * inv_a : 0.f;
     }
     wave_sync();
-#pragma unroll
-    for (int bb = 0; bb < kStepBlk; ++bb) {
-      const float gb = wsc[16 + bb];
-      const int i = bb & 3, grp = bb >> 2;
-      const float k_lo = bf16_to_f32(kbs[bb * 128 + 8 * dswz(bb, lane >> 3) + (lane & 7)]);
-      const float k_hi = bf16_to_f32(kbs[bb * 128 + 8 * dswz(bb, 8 + (lane >> 3)) + (lane & 7)]);
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const bool on = (sgn[i] >> (16 * grp + h)) & 1ull;
-        const float gh = on ? gb : 0.f;
-        dq[h][0] += gh * k_lo;
-        dq[h][1] += gh * k_hi;
-      }
-    }
     {
       // this row's column of G: lane (block lane / 4, head lane % 4)
       const int bb = lane >> 2, h = lane & 3, i = bb & 3, grp = bb >> 2;
@@ -388,7 +384,17 @@ __global__ __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(4))) v
       const float qv = scr[(4 * c + gq) * 128 + 16 * wv + hl];
       cacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ga, qv, cacc, 0, 0, 0);
     }
-    // lane holds blocks 4gq + e of the step at dim 16 wv + hl
+    // dq~: lane (hl, gq) brings kbar[4c + gq][16 wv + hl] and G[4c + gq][16 nt + hl]
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int bq = 4 * c + gq, dd = 16 * wv + hl;
+      const float kv = bf16_to_f32(kbs[bq * 128 + 8 * dswz(bq, dd >> 3) + (dd & 7)]);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        dacc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, gmat[bq * (kDW * 4) + 16 * nt + hl],
+                                                        dacc[nt], 0, 0, 0);
+    }
+    // cacc: lane holds blocks 4gq + e of the step at dim 16 wv + hl
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int64_t blk = (int64_t)st * kStepBlk + 4 * gq + e;
@@ -396,6 +402,19 @@ __global__ __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(4))) v
         unsafeAtomicAdd(a.dkbar + ((int64_t)b * a.nb_cap + blk) * 128 + 16 * wv + hl, cacc[e]);
     }
     __syncthreads();
+  }
+  // dacc[nt]: lane (hl, gq) holds dims 16 wv + 4 gq + e of pair 16 nt + hl;
+  // regroup by row through the (now free) rotated-query scratch
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) scr[(16 * nt + hl) * 128 + 16 * wv + 4 * gq + e] = dacc[nt][e];
+  __syncthreads();
+  float dq[4][2];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    dq[h][0] = scr[(wv * 4 + h) * 128 + lane];
+    dq[h][1] = scr[(wv * 4 + h) * 128 + 64 + lane];
   }
   // dq_idx: rotate back (angle -p) on the rotated dims; pair (j, j + R/2)
   // lives in lanes j and j + R/2 (R <= 64)
