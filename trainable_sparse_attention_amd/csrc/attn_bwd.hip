@@ -8,7 +8,8 @@
 //   query side, one 64-lane wave per (sequence, query row, KV head), as in
 //   the forward (the hq/hkv query heads of the KV head are the 16 columns
 //   of the MFMA tiles); the row's token set is walked twice in chunks of 32
-//   keys, each chunk's K and V copied into LDS:
+//   keys (cyclically from a phase that grows with the position, as in the
+//   forward), each chunk's K and V copied into LDS:
 //     pass 1: S^T = K Q^T (v_mfma_f32_16x16x32_bf16), per-head log-sum-exp;
 //     pass 2: S^T again, P^T = 2^(S^T log2(e) scale - lse), dP^T = V dO^T,
 //             dS^T = P^T (dP^T - Dsum) with Dsum = <dO, O> per head, and
@@ -17,7 +18,8 @@
 //   the selection transposed: per sequence, the rows that selected each
 //   block, as lists in ascending row order (count, scan, scatter, sort);
 //   key side, one wave per (sequence, KV head, block): the block's r keys
-//   against its rows, 16 (row, head) pairs at a time staged in LDS:
+//   against its rows, 16 (row, head) pairs a step staged in LDS, the next
+//   step's rows in flight while a step is computed:
 //     S = Q K^T and dP = dO V^T (16x16x32), P and dS from the staged lse and
 //     Dsum, then dK^T += Q^T dS and dV^T += dO^T P (v_mfma_f32_16x16x16_bf16,
 //     Q^T and dO^T read transposed from LDS); the rows whose incomplete block
@@ -43,6 +45,11 @@ constexpr int kSortCap = 16384;  // longest block row list sorted in LDS
 
 // chunk c of key row kk at c ^ 2(kk & 7) (rows read straight and transposed)
 __device__ __forceinline__ int bswz(int kk, int c) { return c ^ ((kk & 7) << 1); }
+
+// LDS byte address of a pointer into workgroup memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
+}
 
 __device__ __forceinline__ s16x4 tr16(const unsigned short* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
@@ -73,7 +80,7 @@ struct BwdWs {
 template <int RR>
 __global__ __launch_bounds__(64) void attn_bwd_q_kernel(AttnArgs a, const unsigned short* dout,
                                                         float* dq, float* lse_out,
-                                                        float* dsum_out) {
+                                                        float* dsum_out, int resident) {
   constexpr int SPC = kBwdKeys / RR;
   __shared__ __attribute__((aligned(16))) unsigned short kl[kBwdKeys * 128];
   __shared__ __attribute__((aligned(16))) unsigned short vl[kBwdKeys * 128];
@@ -159,27 +166,39 @@ __global__ __launch_bounds__(64) void attn_bwd_q_kernel(AttnArgs a, const unsign
 
   const float sl2 = a.scale * 1.4426950408889634f;
   const int nch = (nslots + SPC - 1) / SPC;
+  // Chunks are visited cyclically from a phase that grows with the row's
+  // position (and so with the launch order), as in the forward: the
+  // resident waves then read the same narrow window of the history at a
+  // time and share it in the caches.  The phase depends on the position and
+  // the device's occupancy only, so repeated calls sum in the same order.
+  int ph = 0;
+  if (resident > 0 && nch > 0) ph = (int)(((pos * a.hkv + g) * nch / resident) % nch);
+  auto chunk_at = [&](int cc) { return cc + ph < nch ? cc + ph : cc + ph - nch; };
 
   // ---- pass 1: log-sum-exp (base 2) of each head's logits --------------
+  // a running maximum and sum per lane, rescaled once per chunk
   float m = -INFINITY, l = 0.f;
-  for (int c = 0; c < nch; ++c) {
-    const int s = SPC * c;
+  for (int cc = 0; cc < nch; ++cc) {
+    const int s = SPC * chunk_at(cc);
     load_chunk(s, false);
     f32x4 sacc[2];
     rows_times(kl, qb, sacc);
+    float x[8];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (!key_ok(s, 16 * kt + 4 * gq + i)) continue;
-        const float x = sacc[kt][i] * sl2;
-        if (x > m) {
-          l = l * exp2f(m - x) + 1.f;
-          m = x;
-        } else {
-          l += exp2f(x - m);
-        }
-      }
+      for (int i = 0; i < 4; ++i)
+        x[4 * kt + i] = key_ok(s, 16 * kt + 4 * gq + i) ? sacc[kt][i] * sl2 : -INFINITY;
+    float mx = m;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mx = fmaxf(mx, x[j]);
+    if (mx != -INFINITY) {
+      float acc = m == -INFINITY ? 0.f : l * exp2f(m - mx);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc += exp2f(x[j] - mx);
+      l = acc;
+      m = mx;
+    }
     __syncthreads();
   }
   const float mm = xmax(m);
@@ -193,8 +212,8 @@ __global__ __launch_bounds__(64) void attn_bwd_q_kernel(AttnArgs a, const unsign
   f32x4 dqa[8];
 #pragma unroll
   for (int tt = 0; tt < 8; ++tt) dqa[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int c = 0; c < nch; ++c) {
-    const int s = SPC * c;
+  for (int cc = 0; cc < nch; ++cc) {
+    const int s = SPC * chunk_at(cc);
     load_chunk(s, true);
     f32x4 sacc[2], dpacc[2];
     rows_times(kl, qb, sacc);
@@ -346,10 +365,14 @@ __global__ __launch_bounds__(1024) void bwd_sort_kernel(BwdWs w) {
 template <int RR>
 __global__ __launch_bounds__(64) void attn_bwd_kv_kernel(AttnArgs a, const unsigned short* dout,
                                                          BwdWs w, float* dk, float* dv) {
-  __shared__ __attribute__((aligned(16))) unsigned short ql[16 * 128];
-  __shared__ __attribute__((aligned(16))) unsigned short ol[16 * 128];
-  __shared__ float lsel[16], dsl[16];
-  __shared__ int32_t rowl[16];
+  // two step buffers: one step's Q and dO rows are computed on while the
+  // next step's are in flight.  buf[s] holds step buffer s: Q rows, then dO
+  // rows (16 pairs x 256 bytes each).  The compute reads them in inline asm
+  // (the compiler would otherwise wait for the loads into the other buffer
+  // before every read), after an explicit wait for the step's own loads.
+  __shared__ __attribute__((aligned(16))) unsigned short buf[2][2 * 16 * 128];
+  __shared__ __attribute__((aligned(16))) float stat[2][2][16];  // [buffer][lse, Dsum][pair]
+  __shared__ __attribute__((aligned(16))) int32_t rid[2][16];    // list entries of a step
   const int lane = threadIdx.x, hl = lane & 15, gq = lane >> 4;
   int64_t wi = blockIdx.x;
   const int64_t j = wi % w.nbk;
@@ -370,6 +393,7 @@ __global__ __launch_bounds__(64) void attn_bwd_kv_kernel(AttnArgs a, const unsig
   const int ntr = tp1 >= tp0 ? (int)(tp1 - tp0 + 1) : 0;
   const int total = L + ntr;
   if (total == 0) return;
+  const int nsteps = (total + RB - 1) / RB;
   const char* kb = (const char*)a.k + ((int64_t)b * a.hkv + g) * a.n_cap * 256;
   const char* vb = (const char*)a.v + ((int64_t)b * a.hkv + g) * a.n_cap * 256;
   // K and V of the block as B operands: column hl = key hl (zero past RR
@@ -391,80 +415,182 @@ __global__ __launch_bounds__(64) void attn_bwd_kv_kernel(AttnArgs a, const unsig
   for (int tt = 0; tt < 8; ++tt) dka[tt] = dva[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float sl2 = a.scale * 1.4426950408889634f;
   const unsigned short* qg = (const unsigned short*)a.q;
-  for (int n0 = 0; n0 < total; n0 += RB) {
-    // the step's rows (-1: none)
+
+  // A step takes RB rows x G heads = 16 (row, head) pairs; lane hl (of every
+  // lane group) stands for pair hl: row slot hl / G, head g G + hl % G.
+  // The row of pair hl at step n (index within the call's rows; -1: none).
+  auto step_row = [&](int n) -> int32_t {
+    const int k = n * RB + hl / G;
+    if (n >= nsteps || hl / G >= RB || k >= total) return -1;
+    return k < L ? list[k] : (int32_t)(tp0 - a.q_pos0) + (k - L);
+  };
+  // the same from the list entry v that fetch_rows brought for step n
+  auto row_from = [&](int n, int32_t v) -> int32_t {
+    const int k = n * RB + hl / G;
+    if (n >= nsteps || hl / G >= RB || k >= total) return -1;
+    return k < L ? v : (int32_t)(tp0 - a.q_pos0) + (k - L);
+  };
+  // lanes 0..15 copy pair hl's list entry of step n into rid[sl] (any
+  // valid word when the pair has none).  1 vector memory instruction.
+  auto fetch_rows = [&](int n, int sl) {
     if (lane < 16) {
-      int32_t t = -1;
-      if (lane < RB && n0 + lane < total)
-        t = n0 + lane < L ? list[n0 + lane] : (int32_t)(tp0 - a.q_pos0) + (n0 + lane - L);
-      rowl[lane] = t;
+      const int k = n * RB + hl / G;
+      const int32_t* src = L > 0 ? list + (k < L ? k : L - 1) : ob + j;
+      __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)rid[sl], 4, 0, 0);
     }
-    __syncthreads();
-    // pairs 4i + lane / 16 of instruction i: chunk lane & 15 of its Q and dO
-    // rows (zero rows are read from row 0 of the sequence and masked below)
+  };
+  auto pair_index = [&](int32_t t, int pr) -> int64_t {  // (row, head) index
+    return ((int64_t)b * a.n_q + (t >= 0 ? t : 0)) * a.hq + g * G + pr % G;
+  };
+  // the step's Q and dO rows into buffer bf: instruction i moves pairs
+  // 4i + lane / 16 (chunk lane & 15 of each row; absent rows read row 0
+  // of the sequence and are masked later), then lanes 0..15 move their
+  // pair's lse and Dsum.  10 vector memory instructions.
+  auto issue = [&](int32_t t, int bf) {
+    unsigned short* qd = buf[bf];
+    unsigned short* od = buf[bf] + 16 * 128;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int pr = 4 * i + (lane >> 4);
-      const int rr = pr / G;
-      const int32_t t = rr < RB ? rowl[rr] : -1;
-      const int64_t rh = ((int64_t)b * a.n_q + (t >= 0 ? t : 0)) * a.hq + g * G + pr % G;
-      const uint64_t off = (uint64_t)rh * 256 + 16 * bswz(pr, lane & 15);
+      const uint64_t off = (uint64_t)pair_index(__shfl(t, pr), pr) * 256 + 16 * bswz(pr, lane & 15);
       __builtin_amdgcn_global_load_lds((glb_void_t*)((const char*)qg + off),
-                                       (lds_void_t*)(ql + i * 512), 16, 0, 0);
+                                       (lds_void_t*)(qd + i * 512), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((glb_void_t*)((const char*)dout + off),
-                                       (lds_void_t*)(ol + i * 512), 16, 0, 0);
+                                       (lds_void_t*)(od + i * 512), 16, 0, 0);
     }
     if (lane < 16) {
-      const int rr = lane / G;
-      const int32_t t = rr < RB ? rowl[rr] : -1;
-      float x = 0.f, y = 0.f;
-      if (t >= 0) {
-        const int64_t rh = ((int64_t)b * a.n_q + t) * a.hq + g * G + lane % G;
-        x = w.lse[rh];
-        y = w.dsum[rh];
-      }
-      lsel[lane] = x;
-      dsl[lane] = y;
+      const int64_t rh = pair_index(t, hl);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(w.lse + rh), (lds_void_t*)stat[bf][0], 4, 0,
+                                       0);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(w.dsum + rh), (lds_void_t*)stat[bf][1], 4,
+                                       0, 0);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    // S = Q K^T, dP = dO V^T: lane (key hl, pairs 4gq + e)
+  };
+
+  // Pipeline: at step n, the rows of step n + 1 are known (their list
+  // entries were fetched a step earlier), step n + 2's list entries and
+  // step n + 1's rows, lse and Dsum are fetched, then step n is computed
+  // once its own loads (the vector memory instructions before the newest
+  // 11) have landed.  Inside the loop every global read goes straight to
+  // LDS and is read back in inline asm after an explicit wait, so no
+  // register waits on a load in flight.
+  int32_t t_cur = step_row(0);
+  fetch_rows(1, 1);
+  issue(t_cur, 0);
+  for (int n = 0; n < nsteps; ++n) {
+    const int cur = n & 1;
+    int32_t t_n1 = -1;
+    if (n + 1 < nsteps) {
+      // step n + 1's list entries (fetched before step n's 10 loads)
+      int32_t v;
+      asm volatile(
+          "s_waitcnt vmcnt(10)\n"
+          "ds_read_b32 %0, %1\n"
+          "s_waitcnt lgkmcnt(0)\n"
+          : "=&v"(v)
+          : "v"(lds_addr(&rid[(n + 1) & 1][hl]))
+          : "memory");
+      t_n1 = row_from(n + 1, v);
+      fetch_rows(n + 2, n & 1);  // 1 instruction
+      issue(t_n1, cur ^ 1);      // 10
+      asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    const unsigned short* qc = buf[cur];
+    // S = Q K^T, dP = dO V^T: lane (key hl, pairs 4gq + e); A rows = pair
+    // hl, dims 32c + 8gq (the dO rows sit 4096 bytes after the Q rows)
+    s16x8 qa[4], oa[4];
+    f32x4 lsev, dsv;  // lse and Dsum of pairs 4gq + e
+    {
+      uint32_t ad[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ad[c] = lds_addr(qc + hl * 128 + 8 * bswz(hl, 4 * c + gq));
+      const uint32_t as = lds_addr(&stat[cur][0][4 * gq]);
+      asm volatile(
+          "ds_read_b128 %0, %10\n"
+          "ds_read_b128 %1, %11\n"
+          "ds_read_b128 %2, %12\n"
+          "ds_read_b128 %3, %13\n"
+          "ds_read_b128 %4, %10 offset:4096\n"
+          "ds_read_b128 %5, %11 offset:4096\n"
+          "ds_read_b128 %6, %12 offset:4096\n"
+          "ds_read_b128 %7, %13 offset:4096\n"
+          "ds_read_b128 %8, %14\n"
+          "ds_read_b128 %9, %14 offset:64\n"
+          "s_waitcnt lgkmcnt(0)\n"
+          : "=&v"(qa[0]), "=&v"(qa[1]), "=&v"(qa[2]), "=&v"(qa[3]), "=&v"(oa[0]), "=&v"(oa[1]),
+            "=&v"(oa[2]), "=&v"(oa[3]), "=&v"(lsev), "=&v"(dsv)
+          : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(as)
+          : "memory");
+    }
     f32x4 sa = {0.f, 0.f, 0.f, 0.f}, dpa = sa;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const bf16x8 qa = *(const bf16x8*)(ql + hl * 128 + 8 * bswz(hl, 4 * c + gq));
-      const bf16x8 oa = *(const bf16x8*)(ol + hl * 128 + 8 * bswz(hl, 4 * c + gq));
-      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[c], sa, 0, 0, 0);
-      dpa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, vf[c], dpa, 0, 0, 0);
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[c]), kf[c], sa,
+                                                   0, 0, 0);
+      dpa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, oa[c]), vf[c], dpa,
+                                                    0, 0, 0);
     }
     s16x4 pb, db;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int pr = 4 * gq + e, rr = pr / G;
-      const int32_t t = rr < RB ? rowl[rr] : -1;
+      const int32_t t = __shfl(t_cur, pr);
+      const float lse = lsev[e], dsm = dsv[e];
       // a listed row attends the whole block; a tail row the keys up to
       // its own position
-      const bool ok = kin && t >= 0 && (n0 + rr < L || key0 + hl <= a.q_pos0 + t);
-      const float p = ok ? exp2f(sa[e] * sl2 - lsel[pr]) : 0.f;
-      const float d = p * (dpa[e] - dsl[pr]);
+      const bool ok = kin && t >= 0 && (n * RB + rr < L || key0 + hl <= a.q_pos0 + t);
+      const float p = ok ? exp2f(sa[e] * sl2 - lse) : 0.f;
+      const float d = p * (dpa[e] - dsm);
       pb[e] = __builtin_bit_cast(short, (__bf16)p);
       db[e] = __builtin_bit_cast(short, (__bf16)d);
     }
     // dK^T += Q^T dS, dV^T += dO^T P: A = Q^T / dO^T read transposed (dims
     // 16tt + hl, pairs 4gq .. 4gq + 3), B = dS / P (pairs, key hl)
+    // (ds_read_b64_tr_b16, as tr16: lane i of a 16-lane group receives
+    // element i % 4 of the 8-byte rows addressed by lanes 4j + i / 4)
     {
       const int kk = 4 * gq + (hl >> 2);
       const int e0 = 4 * (hl & 1);
+      uint32_t ad[8];
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt)
+        ad[tt] = lds_addr(qc + kk * 128 + bswz(kk, 2 * tt + ((hl & 3) >> 1)) * 8 + e0);
+      s16x4 qt[8], ot[8];
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %16\n"
+          "ds_read_b64_tr_b16 %1, %17\n"
+          "ds_read_b64_tr_b16 %2, %18\n"
+          "ds_read_b64_tr_b16 %3, %19\n"
+          "ds_read_b64_tr_b16 %4, %20\n"
+          "ds_read_b64_tr_b16 %5, %21\n"
+          "ds_read_b64_tr_b16 %6, %22\n"
+          "ds_read_b64_tr_b16 %7, %23\n"
+          "ds_read_b64_tr_b16 %8, %16 offset:4096\n"
+          "ds_read_b64_tr_b16 %9, %17 offset:4096\n"
+          "ds_read_b64_tr_b16 %10, %18 offset:4096\n"
+          "ds_read_b64_tr_b16 %11, %19 offset:4096\n"
+          "ds_read_b64_tr_b16 %12, %20 offset:4096\n"
+          "ds_read_b64_tr_b16 %13, %21 offset:4096\n"
+          "ds_read_b64_tr_b16 %14, %22 offset:4096\n"
+          "ds_read_b64_tr_b16 %15, %23 offset:4096\n"
+          "s_waitcnt lgkmcnt(0)\n"
+          : "=&v"(qt[0]), "=&v"(qt[1]), "=&v"(qt[2]), "=&v"(qt[3]), "=&v"(qt[4]), "=&v"(qt[5]),
+            "=&v"(qt[6]), "=&v"(qt[7]), "=&v"(ot[0]), "=&v"(ot[1]), "=&v"(ot[2]), "=&v"(ot[3]),
+            "=&v"(ot[4]), "=&v"(ot[5]), "=&v"(ot[6]), "=&v"(ot[7])
+          : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]),
+            "v"(ad[7])
+          : "memory");
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) {
-        const int ch = 2 * tt + ((hl & 3) >> 1);
-        const s16x4 qt = tr16(ql + kk * 128 + bswz(kk, ch) * 8 + e0);
-        const s16x4 ot = tr16(ol + kk * 128 + bswz(kk, ch) * 8 + e0);
-        dka[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qt, db, dka[tt], 0, 0, 0);
-        dva[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ot, pb, dva[tt], 0, 0, 0);
+        dka[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qt[tt], db, dka[tt], 0, 0, 0);
+        dva[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ot[tt], pb, dva[tt], 0, 0, 0);
       }
     }
-    __syncthreads();
+    t_cur = t_n1;
+    // the next iteration refills this step's buffers
+    __builtin_amdgcn_wave_barrier();
   }
   // dK^T tile tt: lane (key hl, dims 16tt + 4gq + e); one owner per key row
   if (kin) {
@@ -512,12 +638,31 @@ size_t attn_backward_workspace(int B, int n_q, int64_t q_pos0, int hq, int r, in
   return total;
 }
 
+// The period of the query side's chunk phase: its waves resident on the
+// whole device at once (occupancy of the current device), times 0.9 as for
+// the forward (slots refill with a lag).  0 if the query fails: no phase.
+template <int RR>
+static int bwd_resident_waves() {
+  static thread_local int dev_cached = -1, res_cached = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev == dev_cached) return res_cached;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_bwd_q_kernel<RR>, 64, 0) !=
+          hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  dev_cached = dev;
+  res_cached = per_cu * cus * 9 / 10;
+  return res_cached;
+}
+
 template <int RR>
 static hipError_t launch_bwd_r(const AttnArgs& a, const unsigned short* d, float* dq, float* dk,
                                float* dv, const BwdWs& w, hipStream_t st) {
   const int64_t waves = (int64_t)a.B * a.n_q * a.hkv;
   hipLaunchKernelGGL(attn_bwd_q_kernel<RR>, dim3((unsigned)waves), dim3(64), 0, st, a, d, dq,
-                     w.lse, w.dsum);
+                     w.lse, w.dsum, bwd_resident_waves<RR>());
   const int64_t rows = (int64_t)a.B * a.n_q;
   const unsigned cg = (unsigned)((rows + 3) / 4 < 65536 ? (rows + 3) / 4 : 65536);
   const int64_t ncnt = (int64_t)a.B * (w.nbk + 1);
