@@ -472,6 +472,9 @@ def bench_training(args, torch, qsa, inputs, flush):
     c = cnt.to(torch.int64)
     pos = torch.arange(n, device=dev, dtype=torch.int64)
     slots = int(c.sum().item()) * p.r + int(((pos + 1) % p.r).sum().item()) * B
+    # (row, gathered block) pairs of the backward's key side: the selected
+    # blocks and each row's incomplete block
+    bwd_pairs = int(c.sum().item()) + int(((pos + 1) % p.r != 0).sum().item()) * B
     pairs = sum_nb(n, p.r) * B
     causal = B * n * (n + 1) // 2
     # algorithmic work: the teacher's logits once (2 d flops per head and
@@ -480,6 +483,11 @@ def bench_training(args, torch, qsa, inputs, flush):
     # key (logits recomputed, dP, dV, dQ, dK)
     distill_flop = 2.0 * 128 * hq * causal + 3 * 2.0 * 128 * 4 * pairs
     bwd_flop = 10.0 * 128 * hq * slots
+    # algorithmic gathers of the backward: the query side reads each
+    # gathered key's K row twice and its V row once (256 bytes each, per KV
+    # head); the key side reads the Q and dO rows of the KV head's hq / hkv
+    # query heads for every (row, block) pair
+    bwd_gather = 768.0 * slots * hkv + 2 * 256.0 * hq * bwd_pairs
     pool_bwd_bytes = B * (nb * 128 * 4 + n * 128 * 4)
     res = {"workload": inputs.describe("train_32k"), "ms_per_step": ms,
            "stage_ms": {"clear_gradients": st[0], "index_distill": st[1],
@@ -489,15 +497,17 @@ def bench_training(args, torch, qsa, inputs, flush):
                              PEAK_BF16_TFLOPS, "flop": distill_flop},
            "sparse_attn_backward": {"TFLOP/s": bwd_flop / (st[3] * 1e-3) / 1e12,
                                     "frac_mfma": bwd_flop / (st[3] * 1e-3) / 1e12 /
-                                    PEAK_BF16_TFLOPS, "flop": bwd_flop, "sum_T": slots},
+                                    PEAK_BF16_TFLOPS, "flop": bwd_flop, "sum_T": slots,
+                                    "gather_bytes": bwd_gather,
+                                    "gather_GB/s": bwd_gather / (st[3] * 1e-3) / 1e9},
            "pool_keys_backward": {"GB/s": pool_bwd_bytes / (st[2] * 1e-3) / 1e9,
                                   "frac_hbm": pool_bwd_bytes / (st[2] * 1e-3) / 1e9 /
                                   PEAK_HBM_GBS},
            "mean_loss": float(loss.mean().item())}
     log("training kernels %s: %.3f ms/step (clear %.3f, distill %.3f = %.1f TFLOP/s, pool bwd "
-        "%.4f, attn bwd %.3f = %.1f TFLOP/s)" % ("train_32k", ms, st[0], st[1],
-                                                 res["index_distill"]["TFLOP/s"], st[2], st[3],
-                                                 res["sparse_attn_backward"]["TFLOP/s"]))
+        "%.4f, attn bwd %.3f = %.1f TFLOP/s, %.0f GB/s of gathers)" % (
+            "train_32k", ms, st[0], st[1], res["index_distill"]["TFLOP/s"], st[2], st[3],
+            res["sparse_attn_backward"]["TFLOP/s"], res["sparse_attn_backward"]["gather_GB/s"]))
     return res
 
 
