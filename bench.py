@@ -448,9 +448,10 @@ def bench_training(args, torch, qsa, inputs, flush):
     dk = torch.empty((B, hkv, n, 128), dtype=torch.float32, device=dev)
     dv = torch.empty_like(dk)
     wsb = qsa.workspace(qsa.qsa_sparse_attn_backward_workspace(p, B, n, 0, hq))
+    wsd = qsa.workspace(qsa.qsa_index_distill_workspace(p, B, n, 0))
     stages = [lambda: (dkbar.zero_(), dk.zero_(), dv.zero_()),
               lambda: qsa.qsa_index_distill(p, d["q"], d["k"], d["q_idx"], kbar, loss, dq_idx,
-                                            dkbar, 0, 0.0, stream),
+                                            dkbar, wsd, 0, 0.0, stream),
               lambda: qsa.qsa_pool_keys_backward(p, dkbar, dk_idx, 0, nb, stream),
               lambda: qsa.qsa_sparse_attn_backward(p, d["q"], d["k"], d["v"], idx, cnt, out,
                                                    dout, dq, dk, dv, wsb, 0, 0.0, stream)]

@@ -322,14 +322,24 @@ size_t qsa_sparse_attn_backward_workspace(const qsa_params* p, int32_t B, int32_
  *   bfloat16; loss : [B][n_q], dq_idx : [B][n_q][4][128], dkbar :
  *   [B][nb_cap][128], all float32.  Built for r = 4, rope_dims <= 64,
  *   hq <= 16, hkv <= 8, d = 128.
+ *   workspace : device scratch of qsa_index_distill_workspace(...) bytes,
+ *   owned by the caller: the teacher's block values a_b of every row, kept
+ *   from the normaliser pass for the gradient pass (which then needs
+ *   neither the keys nor the teacher's logits).  Needs no clearing.
  * Errors: NULL pointers; positions beyond n_cap or seeing more than nb_cap
- * blocks -> QSA_ERR_SHAPE; other dtypes or sizes -> QSA_ERR_UNSUPPORTED.
+ * blocks -> QSA_ERR_SHAPE; other dtypes or sizes -> QSA_ERR_UNSUPPORTED;
+ * workspace too small -> QSA_ERR_WORKSPACE.
  */
 qsa_status qsa_index_distill(const qsa_params* p, qsa_dtype dtype, const void* q, const void* k,
                              int64_t n_cap, const void* q_idx, const void* kbar, int64_t nb_cap,
                              int32_t B, int32_t n_q, int64_t q_pos0, int32_t hq, int32_t hkv,
                              int32_t d, float scale, float* loss, float* dq_idx, float* dkbar,
-                             void* stream);
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes qsa_index_distill needs: 4 bytes per (sequence, row,
+ * visible block) of the call's rows, i.e. B * sum over positions p of
+ * floor((p+1)/4) (0 for invalid parameters). */
+size_t qsa_index_distill_workspace(const qsa_params* p, int32_t B, int32_t n_q, int64_t q_pos0);
 
 /*
  * qsa_pool_keys_backward -- gradient of the raw indexer keys from the

@@ -136,3 +136,18 @@ def test_workspace_sizes_grow_with_work():
     d = qsa.qsa_index_topk_workspace(p, 1, 8, 1, 1 << 18, True)
     assert d >= 8 * (1 << 18) * 4  # one score per block per sequence
     assert qsa.qsa_sparse_attn_decode_workspace(p, 8, 1, 16, 2) > 0
+    # distillation: one float per (sequence, row, visible block), rows packed
+    for B, n_q, q_pos0 in ((1, 1, 0), (2, 37, 5), (3, 1000, 4093), (1, 4096, 0)):
+        blocks = sum((q + 1) // 4 for q in range(q_pos0, q_pos0 + n_q))
+        assert qsa.qsa_index_distill_workspace(p, B, n_q, q_pos0) == B * blocks * 4
+
+
+def test_distill_rejects_small_workspace():
+    lib = qsa.lib()
+    p = qsa.params()
+    fake = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    need = qsa.qsa_index_distill_workspace(p, 1, 64, 0)
+    assert need > 0
+    for ws, nbytes in ((None, 0), (fake, need - 4)):
+        _expect(lib.qsa_index_distill(ctypes.byref(p), 1, fake, fake, 64, fake, fake, 16, 1, 64, 0,
+                                      16, 2, 128, 0.0, fake, fake, fake, ws, nbytes, None), 5, lib)

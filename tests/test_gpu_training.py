@@ -107,7 +107,10 @@ def test_index_distill(n, q_pos0, hq, hkv):
     loss = torch.full((B, n_q), -1.0, dtype=torch.float32, device="cuda")
     dq = torch.empty((B, n_q, 4, 128), dtype=torch.float32, device="cuda")
     dkb = torch.zeros((B, nb, 128), dtype=torch.float32, device="cuda")
-    qsa.qsa_index_distill(p, qq, t["k"], qi, kbar, loss, dq, dkb, q_pos0)
+    # the workspace needs no clearing: start it as NaN bit patterns
+    ws = qsa.workspace(qsa.qsa_index_distill_workspace(p, B, n_q, q_pos0))
+    ws.fill_(255)
+    qsa.qsa_index_distill(p, qq, t["k"], qi, kbar, loss, dq, dkb, ws, q_pos0)
     # the pooled-key gradient carried to the raw indexer keys
     dk_idx = torch.zeros((B, n, 128), dtype=torch.float32, device="cuda")
     qsa.qsa_pool_keys_backward(p, dkb, dk_idx, 0, nb)

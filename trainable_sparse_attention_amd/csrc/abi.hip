@@ -413,11 +413,16 @@ size_t qsa_sparse_attn_backward_workspace(const qsa_params* p, int32_t B, int32_
   return attn_backward_workspace(B, n_q, q_pos0, hq, p->r, qsa_k_blocks(p));
 }
 
+size_t qsa_index_distill_workspace(const qsa_params* p, int32_t B, int32_t n_q, int64_t q_pos0) {
+  if (!p || p->r != 4 || B < 0 || n_q < 1 || q_pos0 < 0) return 0;
+  return (size_t)B * (size_t)distill_blocks(q_pos0, n_q) * sizeof(float);
+}
+
 qsa_status qsa_index_distill(const qsa_params* p, qsa_dtype dtype, const void* q, const void* k,
                              int64_t n_cap, const void* q_idx, const void* kbar, int64_t nb_cap,
                              int32_t B, int32_t n_q, int64_t q_pos0, int32_t hq, int32_t hkv,
                              int32_t d, float scale, float* loss, float* dq_idx, float* dkbar,
-                             void* stream) {
+                             void* workspace, size_t workspace_bytes, void* stream) {
   qsa_status s = check_params(p);
   if (s) return s;
   if ((s = check_dtype(dtype))) return s;
@@ -440,6 +445,9 @@ qsa_status qsa_index_distill(const qsa_params* p, qsa_dtype dtype, const void* q
   if (n_cap > kMaxCapBf16 || q_pos0 + n_q > (int64_t)0x7fffffff)
     return fail(QSA_ERR_UNSUPPORTED, "n_cap beyond %lld", (long long)kMaxCapBf16);
   if (B == 0) return QSA_OK;
+  const size_t need = qsa_index_distill_workspace(p, B, n_q, q_pos0);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(QSA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   DistillArgs a;
   a.q = (const unsigned short*)q;
   a.k = (const unsigned short*)k;
@@ -448,6 +456,8 @@ qsa_status qsa_index_distill(const qsa_params* p, qsa_dtype dtype, const void* q
   a.loss = loss;
   a.dq_idx = dq_idx;
   a.dkbar = dkbar;
+  a.aws = (float*)workspace;
+  a.aws_ld = distill_blocks(q_pos0, n_q);
   a.n_cap = n_cap;
   a.nb_cap = nb_cap;
   a.q_pos0 = q_pos0;

@@ -21,8 +21,9 @@
 // within a lane quad.  Student scores on the same MFMA with the rotated
 // indexer queries carried as bf16 hi + lo (float-level accuracy).  Three
 // passes over the history: the teacher's log-sum-exp per head; the
-// normalisers (sum of a_b, the student's log-sum-exp) and the loss; the
-// gradients.  Both gradients of a step are small float matrix products with
+// normalisers (sum of a_b, the student's log-sum-exp) and the loss, with
+// every a_b stored to a workspace; the gradients, which read a_b back and
+// so stage only the pooled keys and recompute only the student.  Both gradients of a step are small float matrix products with
 // the step's g values over the workgroup's (row, head) pairs: dkbar of the
 // step's blocks (the rotated queries stay in LDS), added to global memory
 // with float atomics, and dq~, kept in registers.
@@ -67,6 +68,13 @@ __device__ __forceinline__ float xsum4(float x) {  // over lanes hl = 0..3 of a 
 __device__ __forceinline__ float xmax4(float x) {  // over lanes hl = 0..3 of a group
   x = fmaxf(x, __shfl_xor(x, 1));
   return fmaxf(x, __shfl_xor(x, 2));
+}
+// sum over j = 1 .. P of floor(j / 4): the blocks visible to positions
+// 0 .. P - 1 together (r = 4), so that a row's a_b start at
+// blocks_upto(p) - blocks_upto(q_pos0) in the packed workspace
+__host__ __device__ __forceinline__ int64_t blocks_upto(int64_t P) {
+  const int64_t Q = P >> 2, R = P & 3;
+  return 2 * Q * (Q - 1) + Q * (R + 1);
 }
 __device__ __forceinline__ float sel4(const float* v, int i) {  // v[i] without scratch
   return i == 0 ? v[0] : (i == 1 ? v[1] : (i == 2 ? v[2] : v[3]));
@@ -167,8 +175,8 @@ __global__ __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(4))) v
   __syncthreads();
 
   // ---- a step's K rows (every KV head) and pooled keys into LDS ---------
-  const int nkv_ins = hkv * kStepKeys / 4;  // 1 KB instructions for K
-  auto stage = [&](int64_t k0, int64_t klim, bool with_kbar) {
+  auto stage = [&](int64_t k0, int64_t klim, bool with_k, bool with_kbar) {
+    const int nkv_ins = with_k ? hkv * kStepKeys / 4 : 0;  // 1 KB instructions for K
     const int nins = nkv_ins + (with_kbar ? kStepBlk / 4 : 0);
     for (int ins = wv; ins < nins; ins += kDW) {
       if (ins < nkv_ins) {
@@ -228,7 +236,7 @@ __global__ __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(4))) v
   const int nstep1 = (int)((pos_last + 1 + kStepKeys - 1) / kStepKeys);
   for (int st = 0; st < nstep1; ++st) {
     const int64_t k0 = (int64_t)st * kStepKeys;
-    stage(k0, pos_last + 1, false);
+    stage(k0, pos_last + 1, true, false);
     float x[4][4];  // [key tile][head], future keys at -inf
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -259,9 +267,28 @@ __global__ __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(4))) v
     lse[i] = mm == -INFINITY ? -INFINITY : mm + log2f(l);
   }
 
+  float* wsc = wscr + wv * 32;  // this wave's [16] a values, then [16] g values
+  // student: 16 blocks x 4 heads (columns hl < 4); lane (hl, gq) ends with
+  // I of blocks 4gq + i and the sign bits of the 4 heads
+  auto student_terms = [&](float* iv, uint64_t* sgn) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int bb = hl;  // A row: block hl of the step
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const bf16x8 kv = *(const bf16x8*)(kbs + bb * 128 + 8 * dswz(bb, 4 * cc + gq));
+      if (cc < 2 && R > 0)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, ibl[cc], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, ib[cc], acc, 0, 0, 0);
+    }
+    // lane (hl, gq) holds <q~^hl, kbar> of blocks 4gq + i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sgn[i] = __ballot(hl < 4 && acc[i] > 0.f);
+      iv[i] = xsum4(hl < 4 ? relu(acc[i]) : 0.f);
+    }
+  };
   // per step: a_b and I_b of the step's 16 blocks; lane (hl, gq) ends with
   // a and I of blocks 4gq + i (i < 4) and the sign bits of the 4 heads
-  float* wsc = wscr + wv * 32;  // this wave's [16] a values, then [16] g values
   auto block_terms = [&](int64_t k0, float* av, float* iv, uint64_t* sgn) {
     // teacher: head-summed probabilities, maximum over the block's 4 keys
 #pragma unroll
@@ -280,32 +307,21 @@ __global__ __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(4))) v
       if (lane < 16 && (hl & 3) == 0) wsc[4 * kt + (hl >> 2)] = mx;
     }
     wave_sync();
-    // student: 16 blocks x 4 heads (columns hl < 4)
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const int bb = hl;  // A row: block hl of the step
+    student_terms(iv, sgn);
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const bf16x8 kv = *(const bf16x8*)(kbs + bb * 128 + 8 * dswz(bb, 4 * cc + gq));
-      if (cc < 2 && R > 0)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, ibl[cc], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, ib[cc], acc, 0, 0, 0);
-    }
-    // lane (hl, gq) holds <q~^hl, kbar> of blocks 4gq + i
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sgn[i] = __ballot(hl < 4 && acc[i] > 0.f);
-      iv[i] = xsum4(hl < 4 ? relu(acc[i]) : 0.f);
-      av[i] = wsc[4 * gq + i];
-    }
+    for (int i = 0; i < 4; ++i) av[i] = wsc[4 * gq + i];
     wave_sync();
   };
+
 
   // ---- pass 2: normalisers and the loss ----------------------------------
   const int nstep2 = (int)((nb_last + kStepBlk - 1) / kStepBlk);
   float asum = 0.f, alog = 0.f, aI = 0.f, zm = -INFINITY, zl = 0.f;
+  // this row's a_b, blocks 0 .. nb - 1, in the workspace (rows packed)
+  float* const arow = a.aws + (int64_t)b * a.aws_ld + (blocks_upto(pos) - blocks_upto(a.q_pos0));
   for (int st = 0; st < nstep2; ++st) {
     const int64_t k0 = (int64_t)st * kStepKeys;
-    stage(k0, pos_last + 1, true);
+    stage(k0, pos_last + 1, true, true);
     float av[4], iv[4];
     uint64_t sgn[4];
     block_terms(k0, av, iv, sgn);
@@ -314,6 +330,7 @@ __global__ __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(4))) v
       const float ab = sel4(av, hl), ib_ = sel4(iv, hl);
       const int64_t blk = (int64_t)st * kStepBlk + 4 * gq + hl;
       if (blk < nb) {
+        arow[blk] = ab;
         asum += ab;
         alog += ab > 0.f ? ab * logf(ab) : 0.f;
         aI += ab * ib_;
@@ -358,15 +375,16 @@ __global__ __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(4))) v
   const float inv_a = has ? 1.f / asum : 0.f;
   for (int st = 0; st < nstep2; ++st) {
     const int64_t k0 = (int64_t)st * kStepKeys;
-    stage(k0, pos_last + 1, true);
-    float av[4], iv[4];
+    stage(k0, pos_last + 1, false, true);  // the pooled keys only
+    float iv[4];
     uint64_t sgn[4];
-    block_terms(k0, av, iv, sgn);
-    // g of block 4 gq + hl (lanes hl < 4), shared through the wave's scratch
+    student_terms(iv, sgn);
+    // g of block 4 gq + hl (lanes hl < 4, which stored its a_b in pass 2),
+    // shared through the wave's scratch
     if (hl < 4) {
       const int64_t blk = (int64_t)st * kStepBlk + 4 * gq + hl;
       wsc[16 + 4 * gq + hl] =
-          (has && blk < nb) ? expf(sel4(iv, hl) - lnz) - sel4(av, hl) * inv_a : 0.f;
+          (has && blk < nb) ? expf(sel4(iv, hl) - lnz) - arow[blk] * inv_a : 0.f;
     }
     wave_sync();
     {
@@ -436,6 +454,10 @@ __global__ __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(4))) v
       out[h * 128 + 64 + lane] = dq[h][1];
     }
   }
+}
+
+int64_t distill_blocks(int64_t q_pos0, int n_q) {
+  return blocks_upto(q_pos0 + n_q) - blocks_upto(q_pos0);
 }
 
 size_t distill_lds(int hkv) {

@@ -142,12 +142,16 @@ struct DistillArgs {
   float* loss;                  // [B][n_q]
   float* dq_idx;                // [B][n_q][4][128]
   float* dkbar;                 // [B][nb_cap][128], added to
+  float* aws;                   // [B][aws_ld] teacher block values a_b of each row
+  int64_t aws_ld;               // floats per sequence: the rows' visible blocks
   int64_t n_cap, nb_cap, q_pos0;
   int B, n_q, hq, hkv, R;
   float scale;
   double log2_theta;
 };
 size_t distill_lds(int hkv);
+// visible blocks summed over positions q_pos0 .. q_pos0 + n_q - 1 (r = 4)
+int64_t distill_blocks(int64_t q_pos0, int n_q);
 hipError_t launch_distill(const DistillArgs& a, hipStream_t st);
 // pooling backward: dk rows of blocks [b0, b1) written from dkbar
 hipError_t launch_pool_backward(const float* dkbar, int64_t nb_cap, float* dk, int64_t n_cap,

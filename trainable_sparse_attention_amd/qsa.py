@@ -24,6 +24,7 @@ EXPORTS = ["qsa_default_params", "qsa_k_blocks", "qsa_status_str", "qsa_last_err
            "qsa_sparse_attn_decode_workspace", "qsa_sparse_attn_decode_shared",
            "qsa_sparse_attn_decode_noalloc", "qsa_sparse_attn_backward",
            "qsa_sparse_attn_backward_workspace", "qsa_index_distill",
+           "qsa_index_distill_workspace",
            "qsa_pool_keys_backward",
            "qsa_dense_attn_prefill",
            "qsa_dense_attn_decode", "qsa_dense_attn_decode_workspace",
@@ -94,8 +95,10 @@ def lib():
         L.qsa_sparse_attn_backward_workspace.argtypes = [PP, I32, I32, I64, I32]
         L.qsa_sparse_attn_backward_workspace.restype = SZ
         L.qsa_index_distill.argtypes = [PP, ctypes.c_int, P, P, I64, P, P, I64, I32, I32, I64, I32,
-                                        I32, I32, F, P, P, P, P]
+                                        I32, I32, F, P, P, P, P, SZ, P]
         L.qsa_index_distill.restype = ctypes.c_int
+        L.qsa_index_distill_workspace.argtypes = [PP, I32, I32, I64]
+        L.qsa_index_distill_workspace.restype = SZ
         L.qsa_pool_keys_backward.argtypes = [PP, P, I64, P, I64, I32, I64, I64, P]
         L.qsa_pool_keys_backward.restype = ctypes.c_int
         L.qsa_dense_attn_prefill.argtypes = [ctypes.c_int, P, P, P, I64, I32, I32, I64, I32, I32,
@@ -249,15 +252,22 @@ def qsa_sparse_attn_backward(p, q, k, v, idx, cnt, out, dout, dq, dk, dv, worksp
                                           _stream(stream)))
 
 
-def qsa_index_distill(p, q, k, q_idx, kbar, loss, dq_idx, dkbar, q_pos0=0, scale=0.0,
+def qsa_index_distill_workspace(p, B, n_q, q_pos0=0):
+    return lib().qsa_index_distill_workspace(ctypes.byref(p), B, n_q, q_pos0)
+
+
+def qsa_index_distill(p, q, k, q_idx, kbar, loss, dq_idx, dkbar, workspace, q_pos0=0, scale=0.0,
                       stream=None):
     """Stage-1 distillation of the indexer: loss [B][n_q] and dq_idx
-    [B][n_q][4][128] written, dkbar [B][nb_cap][128] added to (float32)."""
+    [B][n_q][4][128] written, dkbar [B][nb_cap][128] added to (float32);
+    workspace of qsa_index_distill_workspace bytes."""
     B, n_q, hq, d = q.shape
     hkv, n_cap = k.shape[1], k.shape[2]
     _check(lib().qsa_index_distill(ctypes.byref(p), dtype_code(q), _ptr(q), _ptr(k), n_cap,
                                    _ptr(q_idx), _ptr(kbar), kbar.shape[1], B, n_q, q_pos0, hq, hkv,
                                    d, scale, _ptr(loss), _ptr(dq_idx), _ptr(dkbar),
+                                   _ptr(workspace),
+                                   0 if workspace is None else workspace.numel(),
                                    _stream(stream)))
 
 
