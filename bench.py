@@ -73,11 +73,14 @@ def log(*a):
 
 
 class ClockSampler:
-    """Samples the graphics clock of device 0 (amdsmi clock info) every few
-    ms on a host thread while the timed steps run; reports min / median / max
-    MHz of the plausible readings.  Informative only: any failure is
-    recorded, not raised.  The clocks the kernels hold under their own load
-    are read from GRBM counters in separate profiler runs."""
+    """Samples device 0's graphics clock as the power-management firmware
+    reports it (amdsmi GPU metrics: the per-XCD current gfxclk) every few ms
+    on a host thread while the timed steps run, and reports min / median /
+    max MHz of the raw readings.  Informative only, and not the clock the
+    kernels hold: on these parts the firmware's readings lag and sit far
+    below it (157 MHz idle, about 400 MHz under a matrix-multiply load),
+    while the GRBM counters show 1.9-2.4 GHz inside the kernels
+    (profiles/qsa_clock_mfma.md).  Any failure is recorded, not raised."""
 
     def __init__(self):
         self.vals, self.err, self._stop = [], None, None
@@ -89,6 +92,13 @@ class ClockSampler:
         except Exception as e:
             self._smi, self.err = None, str(e)[:120]
 
+    def _read(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+        xs = m.get("current_gfxclks")
+        if not isinstance(xs, (list, tuple)):
+            xs = [m.get("current_gfxclk")]
+        return [x for x in xs if isinstance(x, (int, float)) and x > 0]
+
     def __enter__(self):
         import threading
         self.vals = []
@@ -99,12 +109,7 @@ class ClockSampler:
         def run():
             while not self._stop.is_set():
                 try:
-                    # the SMU's current graphics clock; readings outside a
-                    # plausible range (idle or other clock domains) are dropped
-                    c = self._smi.amdsmi_get_clock_info(self._h, self._smi.AmdSmiClkType.GFX)
-                    x = c.get("clk")
-                    if isinstance(x, (int, float)) and 500 <= x <= 3000:
-                        self.vals.append(x)
+                    self.vals.extend(self._read())
                 except Exception as e:
                     self.err = str(e)[:120]
                     return
@@ -120,10 +125,12 @@ class ClockSampler:
             self._t.join()
 
     def summary(self):
-        v = sorted(x for x in self.vals if isinstance(x, (int, float)))
+        v = sorted(self.vals)
         if not v:
             return {"error": self.err or "no samples"}
-        return {"gfx_mhz_min": v[0], "gfx_mhz_median": v[len(v) // 2], "gfx_mhz_max": v[-1],
+        return {"source": "amdsmi GPU metrics, current gfxclk per XCD (firmware reading, not "
+                          "the kernels' clock; see profiles/qsa_clock_mfma.md)",
+                "gfx_mhz_min": v[0], "gfx_mhz_median": v[len(v) // 2], "gfx_mhz_max": v[-1],
                 "samples": len(v)}
 
 
