@@ -61,14 +61,30 @@ __device__ __forceinline__ float xmax16(float x) {  // over the 16 lanes of a gr
   x = fmaxf(x, __shfl_xor(x, 4));
   return fmaxf(x, __shfl_xor(x, 8));
 }
+// The reductions of the inner loops use DPP quad permutes (lanes l ^ 1,
+// l ^ 2) and the permlane swaps (lanes l ^ 16, l ^ 32), which leave every
+// lane of a pair with the pair's two values (the even row's first), so
+// both lanes combine them in the same order.  No LDS traffic.
+__device__ __forceinline__ float dpp_x1(float x) {  // lane l ^ 1
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_x2(float x) {  // lane l ^ 2
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+}
 __device__ __forceinline__ float xsum4(float x) {  // over lanes hl = 0..3 of a group
-  x += __shfl_xor(x, 1);
-  return x + __shfl_xor(x, 2);
+  x += dpp_x1(x);
+  return x + dpp_x2(x);
 }
 __device__ __forceinline__ float xmax4(float x) {  // over lanes hl = 0..3 of a group
-  x = fmaxf(x, __shfl_xor(x, 1));
-  return fmaxf(x, __shfl_xor(x, 2));
+  x = fmaxf(x, dpp_x1(x));
+  return fmaxf(x, dpp_x2(x));
 }
+// hardware exponential (base 2) for the teacher's probabilities: results
+// below 2^-126 are negligible next to the normalised values they are summed
+// with.  The student's softmax and the loss keep the library functions: the
+// gradient g_b = s_b - t_b is a difference of close values, which a
+// relative error of 1e-6 in s_b would show at the 1e-3 level.
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // sum over j = 1 .. P of floor(j / 4): the blocks visible to positions
 // 0 .. P - 1 together (r = 4), so that a row's a_b start at
 // blocks_upto(p) - blocks_upto(q_pos0) in the packed workspace
@@ -80,12 +96,20 @@ __device__ __forceinline__ float sel4(const float* v, int i) {  // v[i] without 
   return i == 0 ? v[0] : (i == 1 ? v[1] : (i == 2 ? v[2] : v[3]));
 }
 __device__ __forceinline__ float xmaxg(float x) {  // over the 4 lane groups
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 __device__ __forceinline__ float xsumg(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 }  // namespace
@@ -201,8 +225,8 @@ __global__ __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(4))) v
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
-  // teacher logits S = Q K^T of key tile kt (16 keys) of the step, scaled to
-  // log2 units: lane (hl, gq) holds key 16 kt + hl against heads 4 gq + i.
+  // teacher logits S = Q K^T of key tile kt (16 keys) of the step (not yet
+  // scaled): lane (hl, gq) holds key 16 kt + hl against heads 4 gq + i.
   // One product per KV head; each of the lane's heads keeps its own KV
   // head's value (heads >= hq keep 0 and are masked by the callers).
   auto teacher = [&](int kt, f32x4& out) {
@@ -220,8 +244,6 @@ __global__ __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(4))) v
       for (int i = 0; i < 4; ++i)
         if ((4 * gq + i) / G == gg) out[i] = acc[i];
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] *= sl2;
   };
 
   // ---- pass 1: teacher log-sum-exp per head (base 2), keys 0 .. p -------
@@ -244,15 +266,15 @@ __global__ __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(4))) v
       teacher(kt, s);
       const bool ok = live && k0 + 16 * kt + hl <= pos;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[kt][i] = ok ? s[i] : -INFINITY;
+      for (int i = 0; i < 4; ++i) x[kt][i] = ok ? s[i] * sl2 : -INFINITY;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float mx = fmaxf(fmaxf(lm[i], fmaxf(x[0][i], x[1][i])), fmaxf(x[2][i], x[3][i]));
       if (mx != -INFINITY) {
-        float acc = lm[i] == -INFINITY ? 0.f : ll[i] * exp2f(lm[i] - mx);
+        float acc = lm[i] == -INFINITY ? 0.f : ll[i] * fexp2(lm[i] - mx);
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) acc += exp2f(x[kt][i] - mx);
+        for (int kt = 0; kt < 4; ++kt) acc += fexp2(x[kt][i] - mx);
         ll[i] = acc;
         lm[i] = mx;
       }
@@ -299,11 +321,10 @@ __global__ __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(4))) v
       float sum = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        sum += (ok && 4 * gq + i < hq) ? exp2f(s[i] - lse[i]) : 0.f;
+        sum += (ok && 4 * gq + i < hq) ? fexp2(fmaf(s[i], sl2, -lse[i])) : 0.f;
       sum = xsumg(sum);  // all heads of key 16 kt + hl
       // block 4 kt + hl / 4: its 4 keys sit in lanes hl & ~3 .. (hl & ~3) + 3
-      float mx = fmaxf(sum, __shfl_xor(sum, 1));
-      mx = fmaxf(mx, __shfl_xor(mx, 2));
+      const float mx = xmax4(sum);
       if (lane < 16 && (hl & 3) == 0) wsc[4 * kt + (hl >> 2)] = mx;
     }
     wave_sync();
