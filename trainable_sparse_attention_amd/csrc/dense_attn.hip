@@ -255,16 +255,21 @@ __global__ __launch_bounds__(64 * W) void dense_attn_kernel(AttnArgs a, int nspl
       // by more than 2^8 (then the column maximum is formed across lanes)
       if (__ballot(mx > m[c] + 8.f)) {
         const float mn = fmaxf(m[c], wmax16(mx));
-        const float alpha = mn == -INFINITY ? 1.f : exp2f(m[c] - mn);
+        const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[c] - mn);
         l[c] *= alpha;
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt) o[c][tt] = o[c][tt] * alpha;
         m[c] = mn;
       }
-      // l: this lane's share of the column sum (summed across lanes at the end)
+      // l: this lane's share of the column sum (summed across lanes at the
+      // end).  A reference still at -inf here means every value of the lane
+      // is -inf (a finite one would have moved it), so 0 stands in for it.
+      const float mref = m[c] == -INFINITY ? 0.f : m[c];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float pj = sv[j] == -INFINITY ? 0.f : exp2f(sv[j] - m[c]);
+        // hardware v_exp_f32 (exp2f wraps it in a range fix-up): results
+        // below 2^-126 of the reference are negligible in the sums
+        const float pj = __builtin_amdgcn_exp2f(sv[j] - mref);
         l[c] += pj;
         pf[c][j] = (__bf16)pj;
       }
