@@ -128,3 +128,71 @@ def test_index_distill(n, q_pos0, hq, hkv):
         assert np.all(g_loss[b][pos < 3] == 0.0)
         o_dk = oracle.pool_backward(g_dkb[b].astype(np.float64))
         assert rel_err(g_dk[b][:nb * 4], o_dk) <= 1e-6
+
+
+def test_training_full_size_sampled():
+    """The training kernels at the 32K-token workload the bench times, in its
+    launch configuration (B = 1, n = 32768, 16 q / 2 kv heads).  Per row:
+    distillation loss and dq_idx and the backward's dq on sampled rows (the
+    first, the last, around 2048 and 16384, and random ones).  Per key: keys
+    of the last 8 blocks are reached only by rows n - 32 .. n - 1 (selected
+    blocks lie below a row's position and tails start at it), so the
+    oracle over those rows gives their whole dkbar, dk and dv."""
+    say("full-size training kernels, train_32k")
+    d = inputs.make("train_32k", seed=8, backend="torch")
+    p = qsa.params()
+    B, n, hq, hkv = d["B"], d["n"], d["hq"], d["hkv"]
+    nb = n // 4
+    kbar, idx, cnt, out = qsa.prefill(p, d["k_idx"], d["q_idx"], d["q"], d["k"], d["v"])
+    loss = torch.empty((B, n), dtype=torch.float32, device="cuda")
+    dqi = torch.empty((B, n, 4, 128), dtype=torch.float32, device="cuda")
+    dkb = torch.zeros((B, nb, 128), dtype=torch.float32, device="cuda")
+    wsd = qsa.workspace(qsa.qsa_index_distill_workspace(p, B, n, 0))
+    qsa.qsa_index_distill(p, d["q"], d["k"], d["q_idx"], kbar, loss, dqi, dkb, wsd, 0)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9)
+    dout = (torch.randn(out.shape, generator=g, device="cuda") * 0.1).to(torch.bfloat16)
+    dq = torch.empty((B, n, hq, 128), dtype=torch.float32, device="cuda")
+    dk = torch.zeros((B, hkv, n, 128), dtype=torch.float32, device="cuda")
+    dv = torch.zeros_like(dk)
+    wsb = qsa.workspace(qsa.qsa_sparse_attn_backward_workspace(p, B, n, 0, hq))
+    qsa.qsa_sparse_attn_backward(p, d["q"], d["k"], d["v"], idx, cnt, out, dout, dq, dk, dv, wsb,
+                                 0)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    tail = np.arange(n - 32, n)
+    rows = np.unique(np.concatenate([np.arange(6), [2046, 2047, 2048, 16383, 16384], tail,
+                                     rng.choice(n, 16, replace=False)])).astype(np.int64)
+    rt = torch.from_numpy(rows).cuda()
+    q_h, k_h, v_h = to_host(d["q"][0]), to_host(d["k"][0]), to_host(d["v"][0])
+    qi_h, kbar_h = to_host(d["q_idx"][0]), to_host(kbar[0])
+    # distillation: loss and dq_idx per row; dkbar of the last 8 blocks
+    o_loss, o_dq, o_dkb = oracle.distill_rows(q_h[rows], k_h, qi_h[rows], kbar_h, rows)
+    _, _, o_dkb_tail = oracle.distill_rows(q_h[tail], k_h, qi_h[tail], kbar_h, tail)
+    g_loss = loss[0][rt].cpu().numpy()
+    d_loss = float(np.max(np.abs(g_loss - o_loss)))
+    errs = [rel_err(dqi[0][rt].cpu().numpy(), o_dq),
+            rel_err(dkb[0][nb - 8:].cpu().numpy(), o_dkb_tail[nb - 8:])]
+    say("distillation over %d rows: loss max |err| %.2e (max |loss| %.2e), dq_idx %.2e, "
+        "dkbar (last 8 blocks) %.2e" % (rows.size, d_loss, float(np.max(np.abs(o_loss))), *errs))
+    assert max(errs) <= 2e-3
+    # The loss (a KL divergence, >= 0 and small) is a difference of per-row
+    # terms of size ln(blocks) + max I, up to about 20 here.  Each lane sums
+    # at most 512 blocks in float32 (a random-walk error near
+    # sqrt(512) * 2^-24 = 1.3e-6 relative) before the lanes are combined, so
+    # the loss carries an absolute error near 2e-5 even when every term is
+    # right to float32 precision.
+    assert d_loss <= 2e-3 * float(np.max(np.abs(o_loss))) + 2e-5
+    # backward: dq per row; dk, dv of the keys of the last 8 blocks
+    g_idx, g_cnt = to_host(idx[0]), to_host(cnt[0])
+    dout_f = inputs.bf16_bits_to_f32(to_host(dout[0])).astype(np.float64)
+    o_dq, _, _ = oracle.attend_backward(q_h[rows], k_h, v_h, rows, g_idx[rows], g_cnt[rows],
+                                        dout_f[rows])
+    _, o_dk, o_dv = oracle.attend_backward(q_h[tail], k_h, v_h, tail, g_idx[tail], g_cnt[tail],
+                                           dout_f[tail])
+    keys = slice(n - 32, n)
+    errs = [rel_err(dq[0][rt].cpu().numpy(), o_dq),
+            rel_err(dk[0][:, keys].cpu().numpy(), o_dk[:, keys]),
+            rel_err(dv[0][:, keys].cpu().numpy(), o_dv[:, keys])]
+    say("backward over %d rows: dq %.2e; last 32 keys: dk %.2e dv %.2e" % (rows.size, *errs))
+    assert max(errs) <= TOL["bf16"]
