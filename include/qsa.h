@@ -196,8 +196,11 @@ qsa_status qsa_sparse_attn_prefill(const qsa_params* p, qsa_dtype dtype, const v
  * (flash-decoding).  Positions d_seq_len[b] - n_q + t.
  *
  *   q : [B][n_q][hq][d]; k_cache, v_cache : [B][hkv][n_cap][d];
- *   d_seq_len : device int32 [B], includes the new tokens;
- *   idx, cnt : from qsa_index_topk in decode mode; out : [B][n_q][hq][d]
+ *   d_seq_len : device int32 [B], includes the new tokens; each length in
+ *               [n_q, n_cap] (not checked on the host: the values live on
+ *               the device; a length outside reads outside the caches)
+ *   idx, cnt : from qsa_index_topk in decode mode for the same lengths;
+ *   out : [B][n_q][hq][d]
  *   workspace : qsa_sparse_attn_decode_workspace(...) bytes
  * Errors as for the prefill call, plus QSA_ERR_WORKSPACE.
  */
@@ -231,7 +234,8 @@ size_t qsa_sparse_attn_decode_workspace(const qsa_params* p, int32_t B, int32_t 
  * the set is causal for every token.
  *
  *   q : [B][n_q][hq][d]; caches [B][hkv][n_cap][d]; d_seq_len : device
- *   int32 [B] (includes the new tokens); idx : [B][1][k_B]; cnt : [B][1];
+ *   int32 [B] (includes the new tokens; each in [n_q, n_cap], not checked
+ *   on the host); idx : [B][1][k_B]; cnt : [B][1];
  *   out : [B][n_q][hq][d]; workspace : qsa_sparse_attn_decode_workspace
  * Errors as for qsa_sparse_attn_decode.
  */
@@ -378,7 +382,8 @@ qsa_status qsa_dense_attn_prefill(qsa_dtype dtype, const void* q, const void* k,
  * 6(d): decode, batch 4, next_n = 4), split over the context in pieces of
  * 4096 keys and combined.
  *   q : [B][n_q][hq][d]; caches [B][hkv][n_cap][d]; d_seq_len device int32
- *   [B] (includes the new tokens, <= n_cap); out : [B][n_q][hq][d];
+ *   [B] (includes the new tokens; each in [n_q, n_cap], not checked on
+ *   the host); out : [B][n_q][hq][d];
  *   workspace : qsa_dense_attn_decode_workspace(B, n_q, hkv, n_cap) bytes.
  * Errors as for qsa_dense_attn_prefill, plus n_q * hq/hkv > 64 ->
  * QSA_ERR_UNSUPPORTED and a small workspace -> QSA_ERR_WORKSPACE.
