@@ -648,6 +648,21 @@ def main():
                        "ceiling_GB/s": pre["gather_bytes"] / (best["ms"] * 1e-3) / 1e9,
                        "attn_frac_of_ceiling": best["ms"] / attn_ms,
                        "probe_at_attn_config_ms": own["ms"], "probe": probe})
+    # end to end: the step's lower bound over the measured step time, with
+    # the indexer at the MFMA peak, the pooling at the HBM peak and the
+    # attention at the larger of its MFMA time and its gather time
+    idx_b = pre["idx_flop"] / (PEAK_BF16_TFLOPS * 1e12) * 1e3
+    pool_b = pre["pool_bytes"] / (PEAK_HBM_GBS * 1e9) * 1e3
+    attn_mfma_b = pre["attn_flop"] / (PEAK_BF16_TFLOPS * 1e12) * 1e3
+    hbm_form = idx_b + max(attn_mfma_b, pre["gather_bytes"] / (PEAK_HBM_GBS * 1e9) * 1e3) + pool_b
+    e2e = {"t_bound_hbm_form_ms": hbm_form,
+           "note": "the gathers at the HBM peak bound the step above its measured time: "
+                   "most gathers are served by L2 and the memory-side cache"}
+    if "ceiling_ms" in gather:
+        t_bound = idx_b + max(attn_mfma_b, gather["ceiling_ms"]) + pool_b
+        e2e.update({"t_bound_ms": t_bound, "frac": t_bound / pre["ms"],
+                    "gather_term": "the measured gather ceiling (probe, %.3f ms)"
+                                   % gather["ceiling_ms"]})
     roof = dict(bound="mfma", achieved=attn_tflops, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                 frac=attn_tflops / PEAK_BF16_TFLOPS, traffic=gather["l2_miss_bytes"],
                 kernel="sparse_attn_prefill", flop=pre["attn_flop"],
@@ -678,6 +693,7 @@ def main():
                       "stage_ms": dict(zip(["pool_keys", "index_topk", "sparse_attn_prefill"],
                                            pre["stage_ms_unflushed"]))},
         "clocks": pre["clocks"],
+        "end_to_end": e2e,
         "stages": {
             "pool_keys": {"ms": st[0], "GB/s": pre["pool_bytes"] / (st[0] * 1e-3) / 1e9,
                           "frac_hbm": pre["pool_bytes"] / (st[0] * 1e-3) / 1e9 / PEAK_HBM_GBS},
