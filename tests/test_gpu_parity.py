@@ -421,6 +421,31 @@ def test_block_size_variants_prefill(r, dtype, n):
         assert err <= TOL[dtype]
 
 
+@pytest.mark.parametrize("rope_dims", [0, 32])
+def test_rope_dims_variants_prefill(rope_dims):
+    """Partial RoPE on fewer of the 128 indexer dims ([hub] "Key ideas",
+    QSA bullet: the rotation covers only part of the dims): no rotated dim
+    (the bf16 queries are exact, no low part is scored) and 32 (low parts on
+    the first two 16-dim steps only), through the many-row indexer at a
+    length whose later tiles take the sampled threshold; pooled keys and
+    sampled selections against the oracle."""
+    say("rope_dims=%d" % rope_dims)
+    n, K = 20480, 2048
+    p = _params(K=K, rope_dims=rope_dims)
+    d = inputs.small(B=1, n=n, hq=4, hkv=1, dtype="bf16", planted=8, seed=300 + rope_dims)
+    t = _dev_inputs(d)
+    kbar = _pool_gpu(p, t["k_idx"], n // 4)
+    idx, cnt = _index_gpu(p, t["q_idx"], kbar)
+    torch.cuda.synchronize()
+    kbar_h, g_idx, g_cnt = to_host(kbar), to_host(idx), to_host(cnt)
+    ref = as_f64(oracle.pool(d["k_idx"][0], rope_dims=rope_dims))
+    _assert_pooled_close(as_f64(kbar_h[0]), ref, "bf16")
+    rows = _transition_rows(n, qsa.k_blocks(p), 4)
+    near, _, _ = _check_index_rows(0, rows, g_idx, g_cnt, d["q_idx"][0], kbar_h[0], K,
+                                   rope_dims=rope_dims)
+    say("rope_dims=%d: %d rows, %d near-tie blocks" % (rope_dims, len(rows), near))
+
+
 @pytest.mark.parametrize("r,n_q,lens", [(1, 1, (9000, 4097, 2050)), (8, 4, (9000, 9001, 5003)),
                                         (16, 1, (40000, 1999, 16391)),
                                         (2, 4, (9002, 7000, 1027))])
@@ -778,14 +803,14 @@ def test_full_size_decode_sampled(cfg):
 def test_threshold_fallback_rescan():
     """White-box: a tile whose rows see more than 3072 blocks first scores a
     strided sample of m = ceil(16 nbmin / k_B) blocks, u * nbmin // m, where
-    nbmin is what its first row sees; lane u % 32 keeps its two largest
+    nbmin is what its first row sees; lane u % 32 keeps its four largest
     sample scores per row, and the row's threshold is the
     ceil(E + 5 sqrt(E) + 2)-th largest kept value (E = m k_B / visible,
     about 16, so the 38th).  Planting high scores on the first 100 sampled
-    blocks for the last row fills every lane's two slots with planted scores,
-    so the threshold lands among the planted scores and fewer than k_B blocks
-    pass it: the tile is flagged and recomputed by the exact kernel, and the
-    selection must still equal the oracle's."""
+    blocks for the last row puts three or four planted scores in every
+    lane, all of them kept, so the threshold lands among the planted scores
+    and fewer than k_B blocks pass it: the tile is flagged and recomputed by
+    the exact kernel, and the selection must still equal the oracle's."""
     say("threshold fallback")
     n = 20480
     d = inputs.small(B=1, n=n, hq=4, hkv=1, dtype="bf16", seed=77)
@@ -794,7 +819,7 @@ def test_threshold_fallback_rescan():
     nbmin = (row0 + 1) // 4
     m = min(max(-(-16 * nbmin // 512), 64), nbmin)
     sample = [u * nbmin // m for u in range(m)]
-    planted = sample[:100]  # distinct high scores; every lane sees three or more
+    planted = sample[:100]  # distinct high scores; three or four in every lane
     qf = inputs.bf16_bits_to_f32(d["q_idx"][0, i, 0])
     kf = inputs.bf16_bits_to_f32(d["k_idx"][0])
     for u, blk in enumerate(planted):

@@ -10,8 +10,8 @@
 //   1. scan (sample): tiles whose rows see more blocks than a list holds
 //      score a strided sample of m blocks, m = 16 visible / k_B (so that
 //      E = m k_B / visible, the expected number of the row's top-k_B blocks
-//      in the sample, is about 16).  Each lane keeps its two largest sample
-//      scores per row; tau = the j-th largest of those 64 values,
+//      in the sample, is about 16).  Each lane keeps its four largest sample
+//      scores per row; tau = the j-th largest of those 128 values,
 //      j = ceil(E + 5 sqrt(E) + 2): five standard deviations above E, and
 //      never above the j-th largest sample score.  Rows that are not
 //      sampled get tau = 0.
@@ -40,6 +40,7 @@ constexpr int kList = 3072;                // candidate list capacity per row
 constexpr int kBuf = 384;                  // LDS append buffer per wave (16-byte entries)
 constexpr int kGroupTiles = 2048;
 constexpr float kSampleE = 16.f;           // expected top-k_B blocks in a sample
+constexpr int kKeep = 4;                   // sample scores kept per lane and row
 constexpr int kCutWaves = 4;
 constexpr int kScanLds = 2 * kStageBytes + kScanWaves * kBuf * 16;
 
@@ -71,6 +72,17 @@ __device__ __forceinline__ TileGeo tile_geo(const IndexArgs& a, int L, int ntile
   G.ncol = (int)((G.seq_off + last_row + 1) / a.r);
   G.nbmin = (int)((G.seq_off + G.row0 + 1) / a.r);
   return G;
+}
+
+// The lane id recomputed where it is used (v_mbcnt in a volatile asm block,
+// which the compiler cannot merge with an earlier value): the sample pass
+// then keeps no lane-derived value live across its register-heavy query
+// prologue, whose spill would be reloaded, with a wait on every load in
+// flight, inside the block loop.
+__device__ __forceinline__ int fresh_lane_id() {
+  int ln;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+  return ln;
 }
 
 __device__ __forceinline__ int sample_size(int nbmin, int kB) {
@@ -186,7 +198,8 @@ __global__ __launch_bounds__(1024, 1) void index_scan_kernel(IndexArgs a, PipeWs
   // ---- per-lane row state: rows q = 2j + g of the wave -------------------
   const int rbase = G.row0 + 8 * wv;
   const int wave_rows = min(8, a.n_q - rbase);
-  float tau[4], t1[4], t2[4];  // t1 >= t2: the lane's two largest sample scores
+  float tau[4];
+  float tk[4][kKeep];  // tk[j][0] >= tk[j][1] >= ...: the lane's largest sample scores
   // entries appended to rows 2j (cnt_lo) and 2j + 1 (cnt_hi): wave-uniform
   int cnt_lo[4], cnt_hi[4];
   // list of row q = 2j + g starts at lbase0 + 2j kList; row q sees (nb0 + q) / r
@@ -196,7 +209,8 @@ __global__ __launch_bounds__(1024, 1) void index_scan_kernel(IndexArgs a, PipeWs
   for (int j = 0; j < 4; ++j) {
     const int q = 2 * j + g;
     tau[j] = SAMPLE ? 0.f : (q < wave_rows ? w.tau[Lg * kTileRows + 8 * wv + q] : 0.f);
-    t1[j] = t2[j] = 0.f;
+#pragma unroll
+    for (int m = 0; m < kKeep; ++m) tk[j][m] = 0.f;
     cnt_lo[j] = cnt_hi[j] = 0;
   }
   // every row of the wave sees blocks below nb_all (0 if some row is absent)
@@ -257,12 +271,16 @@ __global__ __launch_bounds__(1024, 1) void index_scan_kernel(IndexArgs a, PipeWs
           sc[j] = relu(acc[4 * j]) + relu(acc[4 * j + 1]) + relu(acc[4 * j + 2]) +
                   relu(acc[4 * j + 3]);
         if constexpr (SAMPLE) {
+          const bool in = u0 + (fresh_lane_id() & 31) < len;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float v = u < len ? sc[j] : 0.f;
-            const float lo = fminf(v, t1[j]);
-            t1[j] = fmaxf(v, t1[j]);
-            t2[j] = fmaxf(t2[j], lo);
+            float x = in ? sc[j] : 0.f;  // insertion into the sorted kKeep
+#pragma unroll
+            for (int m = 0; m < kKeep; ++m) {
+              const float hi = fmaxf(x, tk[j][m]);
+              x = fminf(x, tk[j][m]);
+              tk[j][m] = hi;
+            }
           }
           continue;
         }
@@ -307,25 +325,25 @@ __global__ __launch_bounds__(1024, 1) void index_scan_kernel(IndexArgs a, PipeWs
     __syncthreads();
   }
   if constexpr (SAMPLE) {
-    // tau of each row from the 64 kept sample scores of its lanes
-    float* tv = (float*)(smem + 2 * kStageBytes) + wv * (8 * 64 + 256);  // [8][64], then hist
-    uint32_t* hist = (uint32_t*)(tv + 8 * 64);
+    // tau of each row from the 32 kKeep kept sample scores of its lanes
+    constexpr int kKept = 32 * kKeep;
+    float* tv = (float*)(smem + 2 * kStageBytes) + wv * (8 * kKept + 256);  // [8][kKept], hist
+    uint32_t* hist = (uint32_t*)(tv + 8 * kKept);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      tv[(2 * j + g) * 64 + 2 * col] = t1[j];
-      tv[(2 * j + g) * 64 + 2 * col + 1] = t2[j];
-    }
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int m = 0; m < kKeep; ++m) tv[(2 * j + g) * kKept + kKeep * col + m] = tk[j][m];
     wave_sync();
     for (int q = 0; q < wave_rows; ++q) {
       const float nvis = (float)((nb0 + q) / a.r);
       const float E = (float)len * (float)a.kB / nvis;
       const int jj = (int)ceilf(E + 5.f * sqrtf(E) + 2.f);
       float thr = 0.f;
-      if (jj <= 64) {
+      if (jj <= kKept) {
         uint32_t v;
         int krem;
-        const uint32_t* tb = (const uint32_t*)(tv + q * 64);
-        wave_radix_kth([&](int e) { return tb[e]; }, 64, jj, hist, lane, &v, &krem);
+        const uint32_t* tb = (const uint32_t*)(tv + q * kKept);
+        wave_radix_kth([&](int e) { return tb[e]; }, kKept, jj, hist, lane, &v, &krem);
         thr = __uint_as_float(v);
       }
       if (lane == 0) w.tau[Lg * kTileRows + 8 * wv + q] = thr;
