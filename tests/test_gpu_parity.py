@@ -330,6 +330,41 @@ def test_decode_parity(n_q, dtype, K, lens):
         assert rel_err(g_out[b], o) <= TOL[dtype]
 
 
+def test_decode_multi_chunk_splits():
+    """A batch large enough that each decode split covers several 32-key
+    chunks (24 sequences x 2 KV heads: 4 chunks per split, 17 splits per
+    row), with 4 new tokens per sequence, 4 query heads and ragged lengths,
+    some below the k_B-block selection (empty splits), and a last split
+    holding only the tail; every sequence's selection and output against
+    the oracle."""
+    say("decode multi-chunk splits")
+    B, n_q = 24, 4
+    rng = np.random.default_rng(61)
+    lens = [int(x) for x in rng.integers(300, 6000, B)]
+    lens[0], lens[1], lens[2] = 6000, 2055, 131
+    n = max(lens)
+    d = inputs.small(B=B, n=n, hq=4, hkv=2, dtype="bf16", seed=61)
+    p = _params()
+    t = _dev_inputs(d)
+    kbar = _pool_gpu(p, t["k_idx"], n // 4)
+    seq_len = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    qi = torch.stack([t["q_idx"][b, L - n_q:L] for b, L in enumerate(lens)]).contiguous()
+    qq = torch.stack([t["q"][b, L - n_q:L] for b, L in enumerate(lens)]).contiguous()
+    idx, cnt = _index_gpu(p, qi, kbar, seq_len=seq_len)
+    out = torch.empty_like(qq)
+    ws = qsa.workspace(qsa.qsa_sparse_attn_decode_workspace(p, B, n_q, 4, 2))
+    qsa.qsa_sparse_attn_decode(p, qq, t["k"], t["v"], seq_len, idx, cnt, out, ws)
+    torch.cuda.synchronize()
+    kbar_h, g_idx, g_cnt, g_out = to_host(kbar), to_host(idx), to_host(cnt), to_host(out)
+    for b, L in enumerate(lens):
+        rows = np.arange(L - n_q, L)
+        o_idx, o_cnt = oracle.index_rows(d["q_idx"][b], kbar_h[b], rows)
+        sc = oracle.score_rows(d["q_idx"][b], kbar_h[b], rows)
+        check_sets(g_idx[b], g_cnt[b], o_idx, o_cnt, sc)
+        o = oracle.attend_rows(d["q"][b], d["k"][b], d["v"][b], rows, g_idx[b], g_cnt[b])
+        assert rel_err(g_out[b], o) <= TOL["bf16"], "sequence %d (length %d)" % (b, L)
+
+
 @pytest.mark.parametrize("n_q,lens", [(4, (9000, 9001, 5003)), (4, (20003, 256, 4098)),
                                       (2, (9002, 7000, 513))])
 def test_decode_shared_selection(n_q, lens):

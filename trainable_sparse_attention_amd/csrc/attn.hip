@@ -149,8 +149,8 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
   const Row R = row_ctx(a, b, t);
   int s0 = 0, s1 = R.nslots;
   if (nsplit > 1) {
-    s0 = split * SPC;
-    s1 = min(R.nslots, s0 + SPC);
+    s0 = split * a.split_slots;
+    s1 = min(R.nslots, s0 + a.split_slots);
   }
   // Block ids of a window of kIdWin slots from `base` (tail slot j is block
   // nb + j; slots past the set read block 0 and are masked).
@@ -404,8 +404,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, int nsplit, fl
   const int r = a.r, spc = kChunkKeys / r;
   int s0 = 0, s1 = R.nslots;
   if (nsplit > 1) {
-    s0 = split * spc;
-    s1 = min(R.nslots, s0 + spc);
+    s0 = split * a.split_slots;
+    s1 = min(R.nslots, s0 + a.split_slots);
   }
   const int G = a.hq / a.hkv;
   const int head = g * G + hl;
@@ -661,10 +661,29 @@ static int max_tail_slots(int r, int n_q, bool shared) {
   const int tail = r - 1 + (shared ? n_q - 1 : 0);
   return (tail + r - 1) / r;
 }
-// A split of the decode attention is one chunk: 32 / r slots.
-static int decode_splits(int kB, int r, int n_q, bool shared) {
+// A split of the decode attention is a run of whole chunks (32 / r slots
+// each): one chunk while a launch for one new token per sequence stays
+// within kDecodeWaves waves, else the fewest chunks (a power of two) that
+// keep it there, so that a large batch writes and merges fewer partials.
+// The count depends on the batch, the KV heads and the selected blocks
+// only: not on the number of new tokens (a token's result does not depend
+// on how many tokens share its call) nor on the tail (the shared-selection
+// form, with more tail slots, never needs fewer splits than the plain one).
+constexpr int64_t kDecodeWaves = 1024;
+static int decode_chunks_per_split(int B, int n_q, int hkv, int kB, int r) {
+  (void)n_q;
   const int spc = kChunkKeys / r;
-  return (kB + max_tail_slots(r, n_q, shared) + spc - 1) / spc;
+  const int64_t rows = (int64_t)B * hkv;
+  const int base = (kB + spc - 1) / spc;
+  int cps = 1;
+  // a split's slots must fit the kernel's slot-id window
+  while (2 * cps * spc + spc <= kIdWin && rows * ((base + cps - 1) / cps) > kDecodeWaves) cps *= 2;
+  return cps;
+}
+static int decode_splits(int B, int n_q, int hkv, int kB, int r, bool shared) {
+  const int spc = kChunkKeys / r;
+  const int slots = spc * decode_chunks_per_split(B, n_q, hkv, kB, r);
+  return (kB + max_tail_slots(r, n_q, shared) + slots - 1) / slots;
 }
 
 template <bool WIN>
@@ -712,7 +731,8 @@ hipError_t launch_attn_prefill(qsa_dtype dt, const AttnArgs& a, hipStream_t st) 
 }
 
 size_t attn_decode_workspace(int B, int n_q, int hkv, int kB, int r, bool shared) {
-  return (size_t)B * n_q * hkv * decode_splits(kB, r, n_q, shared) * kPartFloats * sizeof(float);
+  return (size_t)B * n_q * hkv * decode_splits(B, n_q, hkv, kB, r, shared) * kPartFloats *
+         sizeof(float);
 }
 
 // ---- fixed scratch for the allocation-free decode entry point -------------
@@ -744,8 +764,10 @@ hipError_t attn_static_scratch(void** out) {
   return hipSuccess;
 }
 
-hipError_t launch_attn_decode(qsa_dtype dt, const AttnArgs& a, void* ws, hipStream_t st) {
-  const int nsplit = decode_splits(a.kB, a.r, a.n_q, a.shared);
+hipError_t launch_attn_decode(qsa_dtype dt, const AttnArgs& args, void* ws, hipStream_t st) {
+  AttnArgs a = args;
+  a.split_slots = kChunkKeys / a.r * decode_chunks_per_split(a.B, a.n_q, a.hkv, a.kB, a.r);
+  const int nsplit = decode_splits(a.B, a.n_q, a.hkv, a.kB, a.r, a.shared);
   const int64_t waves = (int64_t)a.B * a.n_q * a.hkv * nsplit;
   if (waves == 0) return hipSuccess;
   float* part = (float*)ws;

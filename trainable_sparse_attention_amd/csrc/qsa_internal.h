@@ -116,6 +116,8 @@ struct AttnArgs {
   // made at the first new token (its tail then runs from that token's block)
   int shared;
   float scale;
+  // decode: slots per split (whole chunks), set by the decode launcher
+  int split_slots;
 };
 
 // split partial per (sequence, token, KV head, split): m[16], l[16],
