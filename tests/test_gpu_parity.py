@@ -330,6 +330,129 @@ def test_decode_parity(n_q, dtype, K, lens):
         assert rel_err(g_out[b], o) <= TOL[dtype]
 
 
+def _random_config(i):
+    """One seeded configuration: micro-block size, indexer heads, rotated
+    dims, K (k_B within the many-row limit), batch, length, chunk offset,
+    attention heads and dtype, drawn independently."""
+    rng = np.random.default_rng(4000 + i)
+    r = int(rng.choice([1, 2, 4, 8, 16]))
+    K = int(rng.choice([64, 256, 1024, 2048, 4096]))
+    while -(-K // r) > 3072:
+        K //= 2
+    hq, hkv = [(4, 1), (8, 2), (16, 2), (6, 3), (16, 16)][int(rng.integers(0, 5))]
+    return dict(r=r, K=K, h=int(rng.choice([1, 2, 4])), R=int(rng.choice([0, 32, 64])),
+                B=int(rng.integers(1, 3)), n=int(rng.integers(200, 14000)),
+                chunk=bool(rng.integers(0, 2)), hq=hq, hkv=hkv,
+                dtype="fp32" if rng.random() < 0.25 else "bf16", seed=4000 + i)
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_configurations(i):
+    """A seeded sweep across the parameters the fixed cases vary one at a
+    time ([hub] "Key ideas", QSA bullet: r, the indexer heads and the
+    rotated share of the dims are the method's parameters; [glide] "QSA
+    Ablations and Efficiency", Figure 5, sweeps r and the head count):
+    pooling, selection and attention of one prefill pass, or of its second
+    half run as a chunk at q_pos0, against the oracle on sampled rows."""
+    c = _random_config(i)
+    say("random configuration %d: %s" % (i, c))
+    r, K, h, R, B, n = c["r"], c["K"], c["h"], c["R"], c["B"], c["n"]
+    p = qsa.params(r=r, K=K, h_idx=h, rope_dims=R)
+    kB = qsa.k_blocks(p)
+    d = inputs.small(B=B, n=n, hq=c["hq"], hkv=c["hkv"], dtype=c["dtype"], r=r, K=K,
+                     seed=c["seed"], planted=4 if n > (kB + 2) * r else 0)
+    q_idx = np.ascontiguousarray(d["q_idx"][:, :, :h])
+    t = _dev_inputs(d)
+    nb = n // r
+    kbar = torch.zeros((B, max(nb, 1), 128), dtype=t["k_idx"].dtype, device="cuda")
+    if nb:
+        qsa.qsa_pool_keys(p, t["k_idx"], kbar, 0, nb)
+    n0 = (n // 3) if c["chunk"] else 0  # rows [n0, n) run as one chunk
+    qi = to_dev(np.ascontiguousarray(q_idx[:, n0:]))
+    qq = t["q"][:, n0:].contiguous()
+    idx, cnt = _index_gpu(p, qi, kbar, q_pos0=n0)
+    out = torch.empty_like(qq)
+    qsa.qsa_sparse_attn_prefill(p, qq, t["k"], t["v"], idx, cnt, out, n0)
+    torch.cuda.synchronize()
+    kbar_h, g_idx, g_cnt, g_out = to_host(kbar), to_host(idx), to_host(cnt), to_host(out)
+    m = n - n0
+    rng = np.random.default_rng(c["seed"])
+    first = kB * r + r - 1 - n0  # first chunk row that sees more than k_B blocks
+    rows = np.concatenate([np.arange(4), np.arange(first - 3, first + 3),
+                           rng.integers(0, m, 48), np.arange(m - 4, m)])
+    rows = np.unique(rows[(rows >= 0) & (rows < m)]).astype(np.int64)
+    for b in range(B):
+        if nb:
+            ref = as_f64(oracle.pool(d["k_idx"][b], r=r, rope_dims=R))
+            _assert_pooled_close(as_f64(kbar_h[b, :nb]), ref, c["dtype"])
+        qb = np.ascontiguousarray(q_idx[b, n0:])
+        o_idx, o_cnt = oracle.index_rows(qb, kbar_h[b], rows, n0, r=r, K=K, rope_dims=R)
+        sc = oracle.score_rows(qb, kbar_h[b], rows, n0, r=r, rope_dims=R)
+        gi, gc = g_idx[b][rows], g_cnt[b][rows]
+        check_sets(gi, gc, o_idx, o_cnt, sc)
+        o = oracle.attend_rows(d["q"][b][n0:], d["k"][b], d["v"][b], rows, gi, gc, n0, r=r)
+        err = rel_err(g_out[b][rows], o)
+        assert err <= TOL[c["dtype"]], "sequence %d: attention error %g" % (b, err)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_decode_configurations(i):
+    """The decode calls over a seeded sweep of batch, new tokens per
+    sequence, ragged lengths (some at or below k_B blocks), micro-block
+    size, indexer heads, rotated dims, K and attention heads ([glide] "QSA
+    Ablations and Efficiency", Figure 6(d): decode with next_n new tokens,
+    and index reuse across them): the selection of every new token, its
+    attention, and the shared-selection attention, against the oracle."""
+    rng = np.random.default_rng(5000 + i)
+    r = int(rng.choice([1, 2, 4, 8, 16]))
+    K = int(rng.choice([64, 256, 2048, 4096]))
+    while -(-K // r) > 4096:
+        K //= 2
+    h, R = int(rng.choice([1, 2, 4])), int(rng.choice([0, 32, 64]))
+    hq, hkv = [(4, 1), (8, 2), (16, 2), (6, 3)][int(rng.integers(0, 4))]
+    B, n_q = int(rng.integers(1, 7)), int(rng.integers(1, 5))
+    lens = [int(x) for x in rng.integers(n_q + r, 12000, B)]
+    say("random decode %d: r=%d K=%d h=%d R=%d heads %d/%d B=%d n_q=%d lens=%s"
+        % (i, r, K, h, R, hq, hkv, B, n_q, lens))
+    n = max(lens)
+    p = qsa.params(r=r, K=K, h_idx=h, rope_dims=R)
+    d = inputs.small(B=B, n=n, hq=hq, hkv=hkv, dtype="bf16", r=r, K=K, seed=5000 + i)
+    q_idx = np.ascontiguousarray(d["q_idx"][:, :, :h])
+    t = _dev_inputs(d)
+    t_qidx = to_dev(q_idx)
+    kbar = torch.empty((B, n // r, 128), dtype=torch.bfloat16, device="cuda")
+    qsa.qsa_pool_keys(p, t["k_idx"], kbar, 0, n // r)
+    seq_len = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    qi = torch.stack([t_qidx[b, L - n_q:L] for b, L in enumerate(lens)]).contiguous()
+    qq = torch.stack([t["q"][b, L - n_q:L] for b, L in enumerate(lens)]).contiguous()
+    idx, cnt = _index_gpu(p, qi, kbar, seq_len=seq_len)
+    ws = qsa.workspace(qsa.qsa_sparse_attn_decode_workspace(p, B, n_q, hq, hkv))
+    out = torch.empty_like(qq)
+    qsa.qsa_sparse_attn_decode(p, qq, t["k"], t["v"], seq_len, idx, cnt, out, ws)
+    first_len = torch.tensor([L - n_q + 1 for L in lens], dtype=torch.int32, device="cuda")
+    sidx, scnt = _index_gpu(p, qi[:, :1].contiguous(), kbar, seq_len=first_len)
+    sout = torch.empty_like(qq)
+    qsa.qsa_sparse_attn_decode_shared(p, qq, t["k"], t["v"], seq_len, sidx, scnt, sout, ws)
+    torch.cuda.synchronize()
+    kbar_h, g_idx, g_cnt, g_out = to_host(kbar), to_host(idx), to_host(cnt), to_host(out)
+    s_idx, s_cnt, s_out = to_host(sidx), to_host(scnt), to_host(sout)
+    for b, L in enumerate(lens):
+        pos = np.arange(L - n_q, L)
+        o_idx, o_cnt = oracle.index_at(q_idx[b][pos], kbar_h[b], pos, r=r, K=K, rope_dims=R)
+        sc = oracle.score_at(q_idx[b][pos], kbar_h[b], pos, r=r, rope_dims=R)
+        check_sets(g_idx[b], g_cnt[b], o_idx, o_cnt, sc)
+        o = oracle.attend_at(d["q"][b][pos], d["k"][b], d["v"][b], pos, g_idx[b], g_cnt[b], r=r)
+        assert rel_err(g_out[b], o) <= TOL["bf16"], "sequence %d" % b
+        f = L - n_q
+        fo_idx, fo_cnt = oracle.index_at(q_idx[b][[f]], kbar_h[b], np.array([f]), r=r, K=K,
+                                         rope_dims=R)
+        fsc = oracle.score_at(q_idx[b][[f]], kbar_h[b], np.array([f]), r=r, rope_dims=R)
+        check_sets(s_idx[b], s_cnt[b], fo_idx, fo_cnt, fsc)
+        os_ = oracle.attend_shared(d["q"][b][pos], d["k"][b], d["v"][b], f, pos, s_idx[b, 0],
+                                   s_cnt[b, 0], r=r)
+        assert rel_err(s_out[b], os_) <= TOL["bf16"], "sequence %d (shared)" % b
+
+
 def test_decode_multi_chunk_splits():
     """A batch large enough that each decode split covers several 32-key
     chunks (24 sequences x 2 KV heads: 4 chunks per split, 17 splits per
