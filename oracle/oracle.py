@@ -61,7 +61,7 @@ def load():
         lib.orc_attend_shared.restype = L
         lib.orc_attend_backward.argtypes = [P, P, P, I, L, L, P, I, I, I, I, I, D, P, P, P, P]
         lib.orc_attend_backward.restype = None
-        lib.orc_distill_row.argtypes = [P, P, I, L, I, I, I, D, P, P, I, I, I, I, D, L, P, P]
+        lib.orc_distill_row.argtypes = [P, P, I, L, I, I, I, D, P, P, I, I, I, I, D, L, P, P, P]
         lib.orc_distill_row.restype = D
         lib.orc_pool_backward.argtypes = [P, I, I, I, D, L, L, P]
         lib.orc_pool_backward.restype = None
@@ -342,12 +342,15 @@ def attend_backward(q_rows, k, v, pos, idx, cnt, dout, r=4, scale=None):
     return dq, dk, dv
 
 
-def distill_rows(q_rows, k, q_idx_rows, kbar, pos, r=4, rope_dims=64, theta=10000.0, scale=None):
+def distill_rows(q_rows, k, q_idx_rows, kbar, pos, r=4, rope_dims=64, theta=10000.0, scale=None,
+                 return_g=False):
     """Indexer distillation of rows given with their positions: per-row KL of
     the indexer's block distribution to the block-max-pooled, head-summed
     dense attention.  q_rows [m][hq][D]; k [hkv][n_cap][D]; q_idx_rows
     [m][h][d] (not rotated); kbar [nb_cap][d] (as stored).  Returns loss [m],
-    dq_idx [m][h][d] and dkbar [nb_cap][d] (float64, summed over the rows)."""
+    dq_idx [m][h][d] and dkbar [nb_cap][d] (float64, summed over the rows);
+    with return_g also g [m][nb_cap], the loss gradient with respect to each
+    visible block's score I_b (zero past the row's visible blocks)."""
     q_rows, k, q_idx_rows, kbar = _c(q_rows), _c(k), _c(q_idx_rows), _c(kbar)
     dt = _dt(q_rows, k, q_idx_rows, kbar)
     m, hq, D = q_rows.shape
@@ -358,13 +361,16 @@ def distill_rows(q_rows, k, q_idx_rows, kbar, pos, r=4, rope_dims=64, theta=1000
     loss = np.zeros(m, dtype=np.float64)
     dq = np.zeros((m, h, d), dtype=np.float64)
     dkbar = np.zeros((kbar.shape[0], d), dtype=np.float64)
+    g = np.zeros((m, kbar.shape[0]), dtype=np.float64)
     esz = 2 if dt == BF16 else 4
     for u in range(m):
         loss[u] = load().orc_distill_row(
             ctypes.c_void_p(q_rows.ctypes.data + u * hq * D * esz), _p(k), dt, n_cap, hq, hkv, D,
             float(scale), ctypes.c_void_p(q_idx_rows.ctypes.data + u * h * d * esz), _p(kbar), h,
             d, r, rope_dims, float(theta), int(pos[u]), dq[u].ctypes.data_as(ctypes.c_void_p),
-            _p(dkbar))
+            _p(dkbar), g[u].ctypes.data_as(ctypes.c_void_p))
+    if return_g:
+        return loss, dq, dkbar, g
     return loss, dq, dkbar
 
 

@@ -479,7 +479,7 @@ void orc_attend_backward(const void* q_row, const void* k, const void* v, int dt
 double orc_distill_row(const void* q_row, const void* k, int dt, int64_t n_cap, int hq,
                        int hkv, int D, double scale, const void* q_idx_row, const void* kbar,
                        int h, int d, int r, int R, double theta, int64_t pos,
-                       double* dq_idx_row, double* dkbar_acc) {
+                       double* dq_idx_row, double* dkbar_acc, double* g_out) {
   int64_t nb = orc_nvis(pos, r);
   for (int c = 0; c < h * d; ++c) dq_idx_row[c] = 0.0;
   if (nb == 0) return 0.0;
@@ -542,6 +542,7 @@ double orc_distill_row(const void* q_row, const void* k, int dt, int64_t n_cap, 
     double ls = I[b] - lz;
     if (t > 0.0) loss += t * (log(t) - ls);
     double gb = exp(ls) - t;
+    if (g_out) g_out[b] = gb; /* d loss / d I_b, for callers that need it */
     for (int hh = 0; hh < h; ++hh) {
       if (!pos_dot[b * h + hh]) continue;
       for (int c = 0; c < d; ++c) {

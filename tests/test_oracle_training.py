@@ -137,7 +137,9 @@ def test_distill_single_head_r1_is_softmax_kl():
 def test_distill_teacher_is_head_sum_block_max():
     """Two attention heads on two KV heads, r = 2: the teacher weight of a
     block is the larger of its two tokens' head-summed probabilities,
-    normalised over the visible blocks -- written out here with numpy."""
+    normalised over the visible blocks -- written out here with numpy.  The
+    loss gradient with respect to each block score, softmax(I) - teacher,
+    is checked from the same numpy terms."""
     rng = np.random.default_rng(38)
     n, D, r, hq, hkv = 26, 128, 2, 2, 2
     q = _grid(rng, (n, hq, D), spread=0.6)
@@ -145,11 +147,11 @@ def test_distill_teacher_is_head_sum_block_max():
     q_idx = _grid(rng, (n, 4, 128), spread=0.2)
     kbar = _grid(rng, (n // r, 128), spread=0.2)
     pos = np.arange(n)
-    L, _, _ = oracle.distill_rows(q, k, q_idx, kbar, pos, r=r)
+    L, _, _, G = oracle.distill_rows(q, k, q_idx, kbar, pos, r=r, return_g=True)
     for i in range(n):
         nb = (i + 1) // r
         if nb == 0:
-            assert L[i] == 0.0
+            assert L[i] == 0.0 and np.all(G[i] == 0.0)
             continue
         ps = np.zeros(i + 1)
         for h in range(hq):
@@ -162,6 +164,8 @@ def test_distill_teacher_is_head_sum_block_max():
         ls = I - (I.max() + np.log(np.exp(I - I.max()).sum()))
         ref = float(np.sum(t * (np.log(t) - ls)))
         assert abs(L[i] - ref) <= 1e-12 + 1e-10 * abs(ref), (i, L[i], ref)
+        assert np.allclose(G[i, :nb], np.exp(ls) - t, rtol=1e-10, atol=1e-14)
+        assert np.all(G[i, nb:] == 0.0)
 
 
 def test_distill_one_visible_block_has_no_loss():
