@@ -296,7 +296,10 @@ def test_bf16_medium_end_to_end_and_chunking():
     (1, "fp32", 2048, (9000, 9001, 5003)), (6, "bf16", 2048, (9000, 9001, 5003)),
     # short sequences (at most 64 pooled blocks: one 16-block tile per scan
     # wave) with k_B = 16, so most rows still select
-    (1, "bf16", 64, (256, 201, 90)), (4, "bf16", 64, (256, 201, 90))])
+    (1, "bf16", 64, (256, 201, 90)), (4, "bf16", 64, (256, 201, 90)),
+    # k_B = 4: selection and tail fit one split, which writes the output
+    # without the merge
+    (1, "bf16", 16, (256, 201, 90)), (4, "fp32", 16, (256, 201, 90))])
 def test_decode_parity(n_q, dtype, K, lens):
     """Ragged sequence lengths; n_q new tokens per sequence (4 = the pages'
     next_n); decode equals the prefill rows at the same positions."""
@@ -730,7 +733,10 @@ def test_dense_prefill(n, q_pos0, n_q, hq, hkv):
 @pytest.mark.parametrize("n_q,lens,hq,hkv", [(1, (9000, 4097, 100), 16, 2),
                                              (4, (9000, 9001, 5003), 16, 2),
                                              (4, (300, 8191, 4096), 8, 2),
-                                             (6, (5000, 2000, 6001), 16, 2)])
+                                             (6, (5000, 2000, 6001), 16, 2),
+                                             # every length within one split
+                                             (2, (3113, 1653, 187), 16, 16),
+                                             (1, (4096, 1000, 5), 8, 2)])
 def test_dense_decode(n_q, lens, hq, hkv):
     say("dense decode n_q=%d lens=%s" % (n_q, lens))
     lens = list(lens)

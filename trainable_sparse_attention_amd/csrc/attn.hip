@@ -777,7 +777,8 @@ hipError_t launch_attn_decode(qsa_dtype dt, const AttnArgs& args, void* ws, hipS
     hipLaunchKernelGGL(attn_f32_kernel, dim3((unsigned)waves), dim3(64), 0, st, a, nsplit, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_attn_combine(dt, a, nsplit, part, st);
+  // one split writes the output itself (no partials to merge)
+  return nsplit > 1 ? launch_attn_combine(dt, a, nsplit, part, st) : hipSuccess;
 }
 
 hipError_t launch_attn_combine(qsa_dtype dt, const AttnArgs& a, int nsplit, const float* part,

@@ -69,7 +69,9 @@ __device__ __forceinline__ float wsum16(float x) {
 }  // namespace
 
 // NCG: 16-column groups per wave; W: waves per workgroup (sharing the K/V
-// stream).  nsplit == 1: prefill; else decode with split_keys keys a split.
+// stream).  part == nullptr: prefill, each column's output written here;
+// else decode: nsplit splits of split_keys keys each write partials to
+// `part` (also when nsplit is 1), merged by the combine kernel.
 template <int NCG, int W>
 __global__ __launch_bounds__(64 * W) void dense_attn_kernel(AttnArgs a, int nsplit,
                                                             int split_keys, float* part) {
@@ -83,7 +85,8 @@ __global__ __launch_bounds__(64 * W) void dense_attn_kernel(AttnArgs a, int nspl
   // ---- work unit --------------------------------------------------------
   int b, g, split = 0, t0;
   int64_t k_lo, k_hi;  // keys [k_lo, k_hi) of this unit
-  if (nsplit == 1) {
+  const bool prefill = part == nullptr;
+  if (prefill) {
     const int tokens = kCols / G;  // query tokens per workgroup
     const int ntiles = (a.n_q + tokens - 1) / tokens;
     int64_t w = blockIdx.x;
@@ -107,7 +110,7 @@ __global__ __launch_bounds__(64 * W) void dense_attn_kernel(AttnArgs a, int nspl
     k_lo = (int64_t)split * split_keys;
     k_hi = min(k_lo + (int64_t)split_keys, L);
   }
-  const int64_t pos0 = nsplit == 1 ? a.q_pos0 : (int64_t)a.seq_len[b] - a.n_q;
+  const int64_t pos0 = prefill ? a.q_pos0 : (int64_t)a.seq_len[b] - a.n_q;
 
   // ---- this lane's columns: token, head, position ------------------------
   // positions stay below 2^31 (checked on the host): 32-bit compares
@@ -118,7 +121,7 @@ __global__ __launch_bounds__(64 * W) void dense_attn_kernel(AttnArgs a, int nspl
     const int col = 16 * (NCG * wv + c) + hl;
     col_t[c] = t0 + col / G;
     col_h[c] = col % G;
-    col_ok[c] = col_t[c] < a.n_q && (nsplit == 1 || col < 16 * NCG);
+    col_ok[c] = col_t[c] < a.n_q && (prefill || col < 16 * NCG);
     col_pos[c] = (int)(pos0 + col_t[c]);
   }
   // every key below this position is visible to all of the wave's columns
@@ -291,7 +294,7 @@ __global__ __launch_bounds__(64 * W) void dense_attn_kernel(AttnArgs a, int nspl
 #pragma unroll
   for (int c = 0; c < NCG; ++c) {
     if (!col_ok[c]) continue;
-    if (nsplit == 1) {
+    if (prefill) {
       const float inv = l[c] > 0.f ? 1.f / l[c] : 0.f;
       unsigned short* orow = (unsigned short*)a.out +
                              (((int64_t)b * a.n_q + col_t[c]) * a.hq + g * G + col_h[c]) * 128;
