@@ -349,6 +349,16 @@ def _random_config(i):
                 dtype="fp32" if rng.random() < 0.25 else "bf16", seed=4000 + i)
 
 
+def _small_k(c, i):
+    """The same configuration with K of a few blocks (at least r tokens): the
+    selection is then shorter than one attention chunk and one decode
+    split."""
+    rng = np.random.default_rng(7000 + i)
+    c = dict(c)
+    c["K"] = max(c["r"], int(rng.choice([1, 8, 16, 32, 48, 100])))
+    return c
+
+
 @pytest.mark.parametrize("i", range(24))
 def test_random_configurations(i):
     """A seeded sweep across the parameters the fixed cases vary one at a
@@ -357,7 +367,16 @@ def test_random_configurations(i):
     Ablations and Efficiency", Figure 5, sweeps r and the head count):
     pooling, selection and attention of one prefill pass, or of its second
     half run as a chunk at q_pos0, against the oracle on sampled rows."""
-    c = _random_config(i)
+    _run_random_prefill(_random_config(i), i)
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_small_k_configurations(i):
+    """The seeded prefill sweep with K of a few blocks."""
+    _run_random_prefill(_small_k(_random_config(i), i), i)
+
+
+def _run_random_prefill(c, i):
     say("random configuration %d: %s" % (i, c))
     r, K, h, R, B, n = c["r"], c["K"], c["h"], c["R"], c["B"], c["n"]
     p = qsa.params(r=r, K=K, h_idx=h, rope_dims=R)
@@ -406,6 +425,17 @@ def test_random_decode_configurations(i):
     Ablations and Efficiency", Figure 6(d): decode with next_n new tokens,
     and index reuse across them): the selection of every new token, its
     attention, and the shared-selection attention, against the oracle."""
+    _run_random_decode(_random_decode_config(i), i)
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_small_k_decode(i):
+    """The seeded decode sweep with K of a few blocks: selection and tail
+    within one attention split for most draws."""
+    _run_random_decode(_small_k(_random_decode_config(i), i), i)
+
+
+def _random_decode_config(i):
     rng = np.random.default_rng(5000 + i)
     r = int(rng.choice([1, 2, 4, 8, 16]))
     K = int(rng.choice([64, 256, 2048, 4096]))
@@ -415,6 +445,12 @@ def test_random_decode_configurations(i):
     hq, hkv = [(4, 1), (8, 2), (16, 2), (6, 3)][int(rng.integers(0, 4))]
     B, n_q = int(rng.integers(1, 7)), int(rng.integers(1, 5))
     lens = [int(x) for x in rng.integers(n_q + r, 12000, B)]
+    return dict(r=r, K=K, h=h, R=R, hq=hq, hkv=hkv, B=B, n_q=n_q, lens=lens)
+
+
+def _run_random_decode(c, i):
+    r, K, h, R, hq, hkv, B, n_q, lens = (c[k] for k in ("r", "K", "h", "R", "hq", "hkv", "B",
+                                                         "n_q", "lens"))
     say("random decode %d: r=%d K=%d h=%d R=%d heads %d/%d B=%d n_q=%d lens=%s"
         % (i, r, K, h, R, hq, hkv, B, n_q, lens))
     n = max(lens)
