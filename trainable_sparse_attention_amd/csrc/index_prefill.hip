@@ -474,7 +474,7 @@ static hipError_t run_pipeline(const IndexArgs& a, const PipeWs& w, int num_cu, 
   const int ntiles = (a.n_q + kTileRows - 1) / kTileRows;
   const int total = ntiles * a.B;
   hipError_t e;
-  if ((e = hipFuncSetAttribute((const void*)index_scan_kernel<NLO, true>,
+  if ((e = hipFuncSetAttribute((const void*)index_scan_kernel<0, true>,
                                hipFuncAttributeMaxDynamicSharedMemorySize, kScanLds)) != hipSuccess)
     return e;
   if ((e = hipFuncSetAttribute((const void*)index_scan_kernel<NLO, false>,
@@ -484,7 +484,10 @@ static hipError_t run_pipeline(const IndexArgs& a, const PipeWs& w, int num_cu, 
     const int gt = total - g0 < w.gt ? total - g0 : w.gt;
     const int nrows = gt * kTileRows;
     const dim3 cg((unsigned)((nrows + kCutWaves - 1) / kCutWaves));
-    hipLaunchKernelGGL((index_scan_kernel<NLO, true>), dim3(gt), dim3(kScanWaves * 64), kScanLds,
+    // The threshold only has to be a value that at least k_B exact scores
+    // reach (the cut checks that, else the row falls back to the exact
+    // kernel), so the sample pass scores with the bf16 query alone.
+    hipLaunchKernelGGL((index_scan_kernel<0, true>), dim3(gt), dim3(kScanWaves * 64), kScanLds,
                        st, a, w, g0, ntiles);
     hipLaunchKernelGGL((index_scan_kernel<NLO, false>), dim3(gt), dim3(kScanWaves * 64), kScanLds,
                        st, a, w, g0, ntiles);
