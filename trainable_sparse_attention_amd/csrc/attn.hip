@@ -119,6 +119,10 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 // chunk c ^ 2(kk & 7), so that a transposed read (16 key rows x two
 // neighbouring chunks) touches every bank exactly twice.
 __device__ __forceinline__ int vswz(int kk, int c) { return c ^ ((kk & 7) << 1); }
+// K chunk layout in LDS: key row kk keeps its 16-byte chunk c at c ^ (kk & 15),
+// so the 16 key rows one operand read touches fall in 16 distinct bank groups.
+__device__ __forceinline__ int kswz(int kk, int c) { return c ^ (kk & 15); }
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i%4
 // of the 8-byte rows addressed by lanes 4j + i/4 (j = 0..3), i.e. a 4 x 16
@@ -140,8 +144,9 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
                                                        int resident) {
   constexpr int SPC = kChunkKeys / RR;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_attn[];
-  unsigned short* vbuf = (unsigned short*)smem_attn;      // [32 keys][128]
-  int* ids = (int*)(smem_attn + 32 * 128 * 2);              // block of each slot
+  unsigned short* vbuf = (unsigned short*)smem_attn;      // V: [32 keys][128]
+  unsigned char* kbuf = smem_attn + 32 * 128 * 2;            // K: [32 keys][256 B]
+  int* ids = (int*)(smem_attn + 2 * 32 * 128 * 2);          // block of each slot
   const int lane = threadIdx.x;
   const int hl = lane & 15, gq = lane >> 4;
   int b, t, g, split;
@@ -188,58 +193,107 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
       qf[cc] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  // The block ids of the chunk at slot s (every slot of a loaded chunk lies
-  // in the window), read as broadcast LDS loads and kept in registers, so
-  // the address math needs no further LDS round trips (r >= 4: one id per
-  // V instruction; below, each lane group reads its own slot's id).
-  constexpr int NID = SPC < 8 ? SPC : 8;
-  auto chunk_ids = [&](int s, int* id) {
-    if constexpr (NID >= 4) {
-      const int4* p = (const int4*)(ids + (s - base));
+  // Block id behind each of a chunk's 8 load instructions (instruction i
+  // moves keys 4i .. 4i + 3), read from the id window in LDS.  The reads are
+  // waited for inside the asm, so no LDS access the compiler sees overlaps
+  // the chunk copies in flight into kbuf / vbuf (it would otherwise wait for
+  // them).  r >= 4: one id covers whole instructions (broadcast reads);
+  // r < 4: each lane group reads the id of its own key.
+  auto chunk_bids = [&](int s, int* bid) {
+    const uint32_t a0 = lds_addr(ids + (s - base));
+    if constexpr (RR == 4) {
+      u32x4 x0, x1;
+      asm volatile(
+          "s_waitcnt lgkmcnt(0)\n"
+          "ds_read_b128 %0, %2\n"
+          "ds_read_b128 %1, %2 offset:16\n"
+          "s_waitcnt lgkmcnt(0)\n"
+          : "=&v"(x0), "=&v"(x1)
+          : "v"(a0)
+          : "memory");
 #pragma unroll
-      for (int j = 0; j < NID / 4; ++j) {
-        const int4 x = p[j];
-        id[4 * j] = x.x; id[4 * j + 1] = x.y; id[4 * j + 2] = x.z; id[4 * j + 3] = x.w;
+      for (int i = 0; i < 4; ++i) {
+        bid[i] = (int)x0[i];
+        bid[4 + i] = (int)x1[i];
       }
+    } else if constexpr (RR == 8) {
+      u32x4 x0;
+      asm volatile(
+          "s_waitcnt lgkmcnt(0)\n"
+          "ds_read_b128 %0, %1\n"
+          "s_waitcnt lgkmcnt(0)\n"
+          : "=&v"(x0)
+          : "v"(a0)
+          : "memory");
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bid[i] = (int)x0[i / 2];
+    } else if constexpr (RR == 16) {
+      u32x2 x0;
+      asm volatile(
+          "s_waitcnt lgkmcnt(0)\n"
+          "ds_read_b64 %0, %1\n"
+          "s_waitcnt lgkmcnt(0)\n"
+          : "=&v"(x0)
+          : "v"(a0)
+          : "memory");
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bid[i] = (int)x0[i / 4];
     } else {
+      // key 4i + lane / 16 is slot (4i + lane / 16) / RR: instruction i's id
+      // sits 4i / RR words past the lane's first
+      const uint32_t al = a0 + 4u * (uint32_t)((lane >> 4) / RR);
+      constexpr int kStep = 16 / RR;  // bytes between instructions' ids
+      uint32_t x[8];
+      asm volatile(
+          "s_waitcnt lgkmcnt(0)\n"
+          "ds_read_b32 %0, %8\n"
+          "ds_read_b32 %1, %8 offset:%9\n"
+          "ds_read_b32 %2, %8 offset:%10\n"
+          "ds_read_b32 %3, %8 offset:%11\n"
+          "ds_read_b32 %4, %8 offset:%12\n"
+          "ds_read_b32 %5, %8 offset:%13\n"
+          "ds_read_b32 %6, %8 offset:%14\n"
+          "ds_read_b32 %7, %8 offset:%15\n"
+          "s_waitcnt lgkmcnt(0)\n"
+          : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+            "=&v"(x[6]), "=&v"(x[7])
+          : "v"(al), "i"(kStep), "i"(2 * kStep), "i"(3 * kStep), "i"(4 * kStep), "i"(5 * kStep),
+            "i"(6 * kStep), "i"(7 * kStep)
+          : "memory");
 #pragma unroll
-      for (int j = 0; j < NID; ++j) id[j] = ids[s - base + j];
+      for (int i = 0; i < 8; ++i) bid[i] = (int)x[i];
     }
-#pragma unroll
-    for (int i = 0; i < NID; ++i) asm volatile("" : "+v"(id[i]));
   };
-  // K operands of a chunk: key row hl of tile kt = key 16kt + hl of the
-  // chunk = slot s + (16kt + hl) / RR, token (16kt + hl) % RR; dims 32cc + 8gq.
-  auto load_k = [&](int s, bf16x8 (*kf)[4]) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int key = 16 * kt + hl;
-      int bid = ids[s - base + key / RR];
-      asm volatile("" : "+v"(bid));
-      const uint32_t off = row_sel(s + key / RR, bid, key % RR) * 256u + 16u * gq;
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) kf[kt][cc] = *(const bf16x8*)(kb + off + 64 * cc);
-    }
-  };
-  // V of a chunk straight into LDS: instruction i moves keys 4i .. 4i + 3
-  // (1 KB); lane l's 16 bytes land at key 4i + l/16, chunk position l%16 of
-  // that key row, so the lane fetches the logical chunk stored there.
-  auto load_v = [&](int s, const int* id, unsigned short* dst) {
+  // One chunk of K or V straight into LDS: instruction i moves keys
+  // 4i .. 4i + 3 (1 KB); lane l's 16 bytes land at key 4i + l/16, chunk
+  // position l%16 of that key row, so the lane fetches the logical chunk the
+  // layout stores there.  Keys outside T_i read row 0 (masked later).
+  auto load_chunk = [&](int s, const int* bid, const char* src, unsigned char* dst, bool isk) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int kk = 4 * i + (lane >> 4);
-      int bid;
-      if constexpr (RR >= 4) {
-        bid = id[4 * i / RR];
-      } else {
-        bid = ids[s - base + kk / RR];
-      }
-      const uint32_t off =
-          row_sel(s + kk / RR, bid, kk % RR) * 256u + 16u * vswz(kk, lane & 15);
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(vb + off), (lds_void_t*)(dst + i * 512), 16,
-                                       0, 0);
+      const int pos = isk ? kswz(kk, lane & 15) : vswz(kk, lane & 15);
+      const uint32_t off = row_sel(s + kk / RR, bid[i], kk % RR) * 256u + 16u * pos;
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(src + off), (lds_void_t*)(dst + i * 1024),
+                                       16, 0, 0);
     }
   };
+  // K operand addresses: key row hl of tile kt (+4096 bytes for kt = 1),
+  // dims 32cc + 8gq .. + 7 = logical chunk 4cc + gq
+  uint32_t ka[4];
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) ka[cc] = lds_addr(kbuf + hl * 256 + 16 * kswz(hl, 4 * cc + gq));
+  // V^T operand addresses (see the PV step)
+  uint32_t va[8];
+  {
+    const int kk = 4 * gq + (hl >> 2);
+    const int e0 = 4 * (hl & 1);
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      const int c = 2 * tt + ((hl & 3) >> 1);
+      va[tt] = lds_addr(vbuf + kk * 128 + vswz(kk, c) * 8 + e0);
+    }
+  }
 
   const float sl2 = a.scale * 1.4426950408889634f;
   f32x4 o[8];
@@ -255,36 +309,71 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
   // the resident waves then read the same narrow window of the history at a
   // time and share it in the caches.  The phase depends on the position, not
   // on the launch index, so a chunked prefill sums in the same order.
-  // A wave loads one chunk (K to registers, V to LDS) and computes it; the
-  // latency is hidden by the other resident waves.
+  // Copies run one chunk ahead, staggered: the next chunk's K is issued once
+  // this chunk's K is in registers, its V once this chunk's V is, so a copy
+  // is in flight while the wave computes.
   const int nch = (s1 - s0 + SPC - 1) / SPC;
   int ph = 0;
   if (!WIN && nsplit == 1 && resident > 0 && nch > 0)
     ph = (int)(((R.pos * a.hkv + g) * nch / resident) % nch);
-  for (int cc = 0; cc < nch; ++cc) {
+  auto slot_of = [&](int cc) {
     int c = ph + cc;
     if (c >= nch) c -= nch;
-    const int s = s0 + SPC * c;
+    return s0 + SPC * c;
+  };
+  // make sure the ids of the chunk at slot s are in the window
+  auto window = [&](int s) {
     if constexpr (WIN) {
       if (s + SPC - base > kIdWin) {
         base = s;
         fill_ids(base);
       }
     }
-    int id[NID];
-    chunk_ids(s, id);
-    bf16x8 kc[2][4];
-    load_k(s, kc);
-    load_v(s, id, vbuf);
+  };
+  int bid[8];
+  if (nch > 0) {
+    const int s = slot_of(0);
+    window(s);
+    chunk_bids(s, bid);
+    load_chunk(s, bid, kb, kbuf, true);
+    load_chunk(s, bid, vb, (unsigned char*)vbuf, false);
+  }
+  for (int cc = 0; cc < nch; ++cc) {
+    const int s = slot_of(cc);
+    const bool more = cc + 1 < nch;
+    // this chunk's K has landed (its V, the 8 newest copies, may not have)
+    u32x4 kr[8];
+    asm volatile(
+        "s_waitcnt vmcnt(8)\n"
+        "ds_read_b128 %0, %8\n"
+        "ds_read_b128 %1, %8 offset:4096\n"
+        "ds_read_b128 %2, %9\n"
+        "ds_read_b128 %3, %9 offset:4096\n"
+        "ds_read_b128 %4, %10\n"
+        "ds_read_b128 %5, %10 offset:4096\n"
+        "ds_read_b128 %6, %11\n"
+        "ds_read_b128 %7, %11 offset:4096\n"
+        "s_waitcnt lgkmcnt(0)\n"
+        : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(kr[2]), "=&v"(kr[3]), "=&v"(kr[4]), "=&v"(kr[5]),
+          "=&v"(kr[6]), "=&v"(kr[7])
+        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3])
+        : "memory");
+    int sn = s;
+    if (more) {
+      sn = slot_of(cc + 1);
+      window(sn);
+      chunk_bids(sn, bid);
+      load_chunk(sn, bid, kb, kbuf, true);
+    }
     // S^T tiles: lane holds head hl, keys 16kt + 4gq + i.
     f32x4 sacc[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
-        sacc[kt] =
-            __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc[kt][cc], qf[cc], sacc[kt], 0, 0, 0);
+      for (int c4 = 0; c4 < 4; ++c4)
+        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, kr[2 * c4 + kt]), qf[c4], sacc[kt], 0, 0, 0);
     }
     // key 16kt + 4gq + i of the chunk: slot s + key / RR, token key % RR
     float sv[8];
@@ -323,44 +412,63 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a, int nsplit, f
     // O^T tile tt: A row = dim 16tt + hl, k index 8gq + j <-> key
     // (j < 4 ? 4gq + j : 16 + 4gq + j - 4), read transposed: lane hl of group
     // gq addresses key 4gq + hl/4 (+16), dims 16tt + 4(hl%4) .. +3.
-    const unsigned short* vs = vbuf;
-    const int kk = 4 * gq + (hl >> 2);
-    const int e0 = 4 * (hl & 1);
-    uint32_t va[8];
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      const int c = 2 * tt + ((hl & 3) >> 1);
-      va[tt] = lds_addr(vs + kk * 128 + vswz(kk, c) * 8 + e0);
-    }
+    // This chunk's V has landed once at most the next chunk's K copies (8)
+    // remain; all of it is read before the next chunk's V is issued.
     s16x4 vr[16];
-    // wait until this chunk's V has landed, then read it all; the reads
-    // complete inside the block, before the next chunk's V is fetched
-    asm volatile(
-        "s_waitcnt vmcnt(0)\n"
-        "s_barrier\n"
-        "ds_read_b64_tr_b16 %0, %16\n"
-        "ds_read_b64_tr_b16 %1, %16 offset:4096\n"
-        "ds_read_b64_tr_b16 %2, %17\n"
-        "ds_read_b64_tr_b16 %3, %17 offset:4096\n"
-        "ds_read_b64_tr_b16 %4, %18\n"
-        "ds_read_b64_tr_b16 %5, %18 offset:4096\n"
-        "ds_read_b64_tr_b16 %6, %19\n"
-        "ds_read_b64_tr_b16 %7, %19 offset:4096\n"
-        "ds_read_b64_tr_b16 %8, %20\n"
-        "ds_read_b64_tr_b16 %9, %20 offset:4096\n"
-        "ds_read_b64_tr_b16 %10, %21\n"
-        "ds_read_b64_tr_b16 %11, %21 offset:4096\n"
-        "ds_read_b64_tr_b16 %12, %22\n"
-        "ds_read_b64_tr_b16 %13, %22 offset:4096\n"
-        "ds_read_b64_tr_b16 %14, %23\n"
-        "ds_read_b64_tr_b16 %15, %23 offset:4096\n"
-        "s_waitcnt lgkmcnt(0)\n"
-        : "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]),
-          "=&v"(vr[6]), "=&v"(vr[7]), "=&v"(vr[8]), "=&v"(vr[9]), "=&v"(vr[10]), "=&v"(vr[11]),
-          "=&v"(vr[12]), "=&v"(vr[13]), "=&v"(vr[14]), "=&v"(vr[15])
-        : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]),
-          "v"(va[7])
-        : "memory");
+    if (more) {
+      asm volatile(
+          "s_waitcnt vmcnt(8)\n"
+          "ds_read_b64_tr_b16 %0, %16\n"
+          "ds_read_b64_tr_b16 %1, %16 offset:4096\n"
+          "ds_read_b64_tr_b16 %2, %17\n"
+          "ds_read_b64_tr_b16 %3, %17 offset:4096\n"
+          "ds_read_b64_tr_b16 %4, %18\n"
+          "ds_read_b64_tr_b16 %5, %18 offset:4096\n"
+          "ds_read_b64_tr_b16 %6, %19\n"
+          "ds_read_b64_tr_b16 %7, %19 offset:4096\n"
+          "ds_read_b64_tr_b16 %8, %20\n"
+          "ds_read_b64_tr_b16 %9, %20 offset:4096\n"
+          "ds_read_b64_tr_b16 %10, %21\n"
+          "ds_read_b64_tr_b16 %11, %21 offset:4096\n"
+          "ds_read_b64_tr_b16 %12, %22\n"
+          "ds_read_b64_tr_b16 %13, %22 offset:4096\n"
+          "ds_read_b64_tr_b16 %14, %23\n"
+          "ds_read_b64_tr_b16 %15, %23 offset:4096\n"
+          "s_waitcnt lgkmcnt(0)\n"
+          : "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]),
+            "=&v"(vr[6]), "=&v"(vr[7]), "=&v"(vr[8]), "=&v"(vr[9]), "=&v"(vr[10]), "=&v"(vr[11]),
+            "=&v"(vr[12]), "=&v"(vr[13]), "=&v"(vr[14]), "=&v"(vr[15])
+          : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]),
+            "v"(va[7])
+          : "memory");
+      load_chunk(sn, bid, vb, (unsigned char*)vbuf, false);
+    } else {
+      asm volatile(
+          "s_waitcnt vmcnt(0)\n"
+          "ds_read_b64_tr_b16 %0, %16\n"
+          "ds_read_b64_tr_b16 %1, %16 offset:4096\n"
+          "ds_read_b64_tr_b16 %2, %17\n"
+          "ds_read_b64_tr_b16 %3, %17 offset:4096\n"
+          "ds_read_b64_tr_b16 %4, %18\n"
+          "ds_read_b64_tr_b16 %5, %18 offset:4096\n"
+          "ds_read_b64_tr_b16 %6, %19\n"
+          "ds_read_b64_tr_b16 %7, %19 offset:4096\n"
+          "ds_read_b64_tr_b16 %8, %20\n"
+          "ds_read_b64_tr_b16 %9, %20 offset:4096\n"
+          "ds_read_b64_tr_b16 %10, %21\n"
+          "ds_read_b64_tr_b16 %11, %21 offset:4096\n"
+          "ds_read_b64_tr_b16 %12, %22\n"
+          "ds_read_b64_tr_b16 %13, %22 offset:4096\n"
+          "ds_read_b64_tr_b16 %14, %23\n"
+          "ds_read_b64_tr_b16 %15, %23 offset:4096\n"
+          "s_waitcnt lgkmcnt(0)\n"
+          : "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]),
+            "=&v"(vr[6]), "=&v"(vr[7]), "=&v"(vr[8]), "=&v"(vr[9]), "=&v"(vr[10]), "=&v"(vr[11]),
+            "=&v"(vr[12]), "=&v"(vr[13]), "=&v"(vr[14]), "=&v"(vr[15])
+          : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]),
+            "v"(va[7])
+          : "memory");
+    }
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
       const s16x8 vv = __builtin_shufflevector(vr[2 * tt], vr[2 * tt + 1], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -604,7 +712,7 @@ __global__ __launch_bounds__(128 * kCombGroups) void attn_combine_kernel(
 }
 
 // LDS the bf16 kernel uses: one V chunk and a window of slot ids.
-static size_t bf16_lds_need() { return 32 * 128 * 2 + (size_t)kIdWin * 4; }
+static size_t bf16_lds_need() { return 2 * 32 * 128 * 2 + (size_t)kIdWin * 4; }
 
 // Waves of the prefill bf16 kernel allowed on one CU.  Fewer concurrent waves
 // keep the window of the history that the resident waves read at one time
