@@ -10,9 +10,10 @@
 // or 16 (the micro-block sizes the pages sweep).
 //
 // bf16: S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 (16 keys x
-//   16 heads per tile, heads beyond hq/hkv are zero); V is staged through
-//   LDS and read transposed for the A operand.  Softmax and accumulation in
-//   float (online, base 2).  P is rounded to bf16 for the PV product.
+//   16 heads per tile, heads beyond hq/hkv are zero); K and V are copied
+//   global -> LDS one chunk ahead of the compute (V read transposed for the
+//   A operand).  Softmax and accumulation in float (online, base 2).  P is
+//   rounded to bf16 for the PV product.
 // fp32: the same on v_mfma_f32_16x16x4f32, whose one-element-per-lane
 //   operands need no transpose (the output dims are permuted instead).
 //
@@ -29,8 +30,6 @@ namespace qsa {
 namespace {
 
 constexpr int kChunkKeys = 32;   // keys per chunk: two 16-key MFMA tiles
-constexpr int kSlotsPerChunk = 8;  // at r = 4
-constexpr int kVRow = 128 + 8;  // LDS row of V in bf16 elements (16 B pad)
 constexpr int kIdWin = 576;     // slot ids staged in LDS at a time (whole chunks)
 
 struct Row {
