@@ -743,10 +743,11 @@ static size_t bf16_lds_prefill() {
 }
 
 // The period of the prefill kernel's chunk phase: the waves resident on the
-// whole device at once, from the occupancy of the current device, times
-// 0.9 (slots refill with a lag; on the 256K-token prefill step, 0.9 and 0.95
-// of the occupancy bound align best: attention 39.2 ms against 39.7 at 1.0,
-// 40.6 at 0.8 and 40.4 at 1.1).
+// whole device at once, from the occupancy of the current device.  With each
+// wave's copies running one chunk ahead, the full occupancy bound aligns
+// best (256K-token prefill, attention: 38.5 ms at 1.0 of the bound, 38.8 at
+// 0.9, 40.5 at 0.8 and at 1.2); with copies issued only when a chunk was
+// computed, 0.9 had (39.2 ms against 39.7 at 1.0).
 static int resident_waves() {
   static thread_local int dev_cached = -1, res_cached = 0;
   int dev = 0;
@@ -758,7 +759,7 @@ static int resident_waves() {
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
   dev_cached = dev;
-  res_cached = per_cu * cus * 9 / 10;
+  res_cached = per_cu * cus;
   return res_cached;
 }
 
